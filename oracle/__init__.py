@@ -1,0 +1,19 @@
+"""CPU oracle for the hybrid-TwELL ReLU FFN forward (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package; the product path never does.
+"""
+from .twell_oracle import (  # noqa: F401
+    Hybrid,
+    bf16_bits_to_f32,
+    ell_pack_textbook,
+    ffn_forward,
+    ffn_forward_rows,
+    ffn_hidden,
+    pack,
+    pack_reference,
+    spmm,
+    tile_counts,
+    to_csr,
+    unpack,
+)
