@@ -1,0 +1,75 @@
+// Host-side launchers of the TwELL kernels (internal to libtwell.so).
+// Every launcher only enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace twell {
+
+// Output side of the TwELL pack step shared by the fused up-projection and
+// the standalone dense_to_twell.
+struct PackOut {
+  void* vals;        // [N][nt][C] dtype
+  uint8_t* idx;      // [N][nt][C]
+  uint8_t* cnt;      // [N][nt]
+  uint8_t* flags;    // [N][nt] workspace: 1 when the tile overflowed
+  void* spill;       // [N][d_ff] workspace or nullptr: raw h of overflowing tiles
+  void* h_debug;     // [N][d_ff] or nullptr: every h element as packed
+};
+
+struct Geometry {
+  int64_t n_rows;
+  int d_model;
+  int d_ff;
+  int tile;
+  int capacity;
+  int n_tiles;
+};
+
+// G1: h = ReLU(x w_up_t^T + b) rounded to dtype, packed per (row, tile).
+hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint16_t* w_up_t,
+                               const float* b_up, const PackOut& out, hipStream_t s);
+hipError_t launch_up_pack_f32(const Geometry& g, const float* x, const float* w_up_t,
+                              const float* b_up, const PackOut& out, hipStream_t s);
+
+// G5 first half: pack an existing h [N][d_ff] per (row, tile).
+hipError_t launch_pack_tiles(const Geometry& g, const void* h, int elem_bytes, const PackOut& out,
+                             hipStream_t s);
+
+// G2a: per-row OR of the tile flags, ascending numbering of dense rows.
+//   row_map[n] = dense index m, or -1 for a sparse row; dense_rows[m] = n for
+//   m < dense_cap; *n_dense = total; *status = OK / DENSE_CAPACITY.
+hipError_t launch_route_scan(const Geometry& g, const uint8_t* flags, int32_t* row_map,
+                             int32_t* dense_rows, int64_t dense_cap, int32_t* n_dense,
+                             int32_t* status, hipStream_t s);
+
+// G2b: dense_values[m] = row n of h (from `full_src` if given, else from the
+// TwELL slots of the row plus the spilled overflowing tiles), then the row's
+// TwELL slots are cleared.
+hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* row_map,
+                              const uint8_t* flags, const void* spill, const void* full_src,
+                              void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
+                              int64_t dense_cap, hipStream_t s);
+
+// G6: twell_to_dense.
+hipError_t launch_unpack(const Geometry& g, int elem_bytes, const void* vals, const uint8_t* idx,
+                         const uint8_t* cnt, const int32_t* dense_rows, const void* dense_values,
+                         const int32_t* n_dense, int64_t dense_cap, void* h, hipStream_t s);
+
+// G3: y[n] = sum of value * w_down[row] over the stored slots of row n, for
+// every row n (rows listed as dense in `row_map`, when given, are skipped).
+hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
+                              const uint8_t* idx, const uint8_t* cnt, const int32_t* row_map,
+                              const void* w_down, void* y, hipStream_t s);
+
+// G4: y[dense_rows[m]] = dense_values[m] w_down for m < min(*n_dense, dense_cap).
+hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
+                                const int32_t* dense_rows, const int32_t* n_dense,
+                                int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
+                                hipStream_t s);
+hipError_t launch_fallback_f32(const Geometry& g, const float* dense_values,
+                               const int32_t* dense_rows, const int32_t* n_dense,
+                               int64_t dense_cap, const float* w_down, float* y, hipStream_t s);
+
+}  // namespace twell

@@ -1,0 +1,290 @@
+// Row routing and the dense <-> TwELL conversions.
+//
+//  G2a route_scan   per-row OR of the tile-overflow flags, ascending numbering
+//                   of the dense rows (one workgroup, block-wide prefix scan,
+//                   so the order is deterministic);
+//  G2b materialize  dense_values[m] = full row of h for each dense row, then
+//                   the row's TwELL slots are cleared;
+//  G5  pack_tiles   dense_to_twell of an existing h, one wave per (row, tile);
+//  G6  unpack       twell_to_dense.
+//
+// Format: "Sparser, Faster, Lighter Transformer Language Models (Sakana AI +
+// NVIDIA)", Figure 1 description (values, tile-local indices, per-tile
+// counts; the hybrid splits rows between TwELL and a dense matrix).  The
+// conversions are the dense-to-TwELL and TwELL-to-dense paths named in
+// "SakanaAI/sparser-faster-llms: How TwELL Makes Sparse Transformers Run Like
+// They Were Built for Hopper", section "TwELL: The Packing Format That Fits
+// the Machine".  Rows go dense as a whole when any tile overflows (the rare
+// dense tokens of "Nvidia and Sakana make LLMs 30% faster by doing less
+// math", section "Reshaping math for the GPU").
+#include "../../include/twell.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace twell {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ bool row_has_flag(const uint8_t* __restrict__ f, int nt) {
+  uint32_t any = 0;
+  if ((nt & 15) == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(f);
+    for (int i = 0; i < nt / 16; ++i) {
+      const uint4 q = p[i];
+      any |= q.x | q.y | q.z | q.w;
+    }
+  } else if ((nt & 3) == 0) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(f);
+    for (int i = 0; i < nt / 4; ++i) any |= p[i];
+  } else {
+    for (int i = 0; i < nt; ++i) any |= f[i];
+  }
+  return any != 0;
+}
+
+// Inclusive scan of one int across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
+    const uint8_t* __restrict__ flags, int64_t N, int nt, int32_t* __restrict__ row_map,
+    int32_t* __restrict__ dense_rows, int64_t cap, int32_t* __restrict__ n_dense,
+    int32_t* __restrict__ status) {
+  __shared__ int wave_tot[kScanThreads / kWave];
+  const int tid = threadIdx.x;
+  const int64_t per = (N + kScanThreads - 1) / kScanThreads;
+  const int64_t r0 = min(N, tid * per), r1 = min(N, r0 + per);
+  int local = 0;
+  for (int64_t n = r0; n < r1; ++n) {
+    const bool d = row_has_flag(flags + n * nt, nt);
+    row_map[n] = d ? 1 : 0;  // re-read below by this same thread
+    local += d;
+  }
+  const int incl = wave_inclusive_scan(local);
+  const int wave = tid / kWave, lane = lane_id();
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < kScanThreads / kWave; ++w) {
+    before += (w < wave) ? wave_tot[w] : 0;
+    total += wave_tot[w];
+  }
+  int m = before + incl - local;  // exclusive prefix of this thread's rows
+  for (int64_t n = r0; n < r1; ++n) {
+    if (row_map[n]) {
+      row_map[n] = m;
+      if (m < cap) dense_rows[m] = static_cast<int32_t>(n);
+      ++m;
+    } else {
+      row_map[n] = -1;
+    }
+  }
+  if (tid == 0) {
+    *n_dense = total;
+    if (status != nullptr) *status = total > cap ? TWELL_ERR_DENSE_CAPACITY : TWELL_OK;
+  }
+}
+
+template <typename E>
+struct Vec16 {
+  static constexpr int N = 16 / sizeof(E);
+  E v[N];
+};
+
+template <typename E>
+__device__ __forceinline__ void load_vec(Vec16<E>& d, const E* p) {
+  *reinterpret_cast<uint4*>(d.v) = *reinterpret_cast<const uint4*>(p);
+}
+template <typename E>
+__device__ __forceinline__ void store_vec(E* p, const Vec16<E>& d) {
+  *reinterpret_cast<uint4*>(p) = *reinterpret_cast<const uint4*>(d.v);
+}
+
+// Columns [c, c + 16/sizeof(E)) of a TwELL row, rebuilt from the slots of
+// tile t: zeros except the stored entries.
+template <typename E>
+__device__ __forceinline__ void gather_tile_vec(Vec16<E>& out, const E* __restrict__ vals,
+                                                const uint8_t* __restrict__ idx, int count, int C,
+                                                int local0) {
+#pragma unroll
+  for (int i = 0; i < Vec16<E>::N; ++i) out.v[i] = E(0);
+  for (int k = 0; k < count && k < C; ++k) {
+    const int d = static_cast<int>(idx[k]) - local0;
+    if (d >= 0 && d < Vec16<E>::N) out.v[d] = vals[k];
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kRowThreads) void materialize_kernel(
+    int dff, int T, int C, int nt, const int32_t* __restrict__ row_map,
+    const uint8_t* __restrict__ flags, const E* __restrict__ spill, const E* __restrict__ full_src,
+    E* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    E* __restrict__ dense_values, int64_t cap) {
+  constexpr int V = Vec16<E>::N;
+  const int64_t n = blockIdx.x;
+  const int m = row_map[n];
+  if (m < 0) return;
+  const int64_t slot0 = n * nt;
+  if (m < cap) {
+    E* dst = dense_values + static_cast<int64_t>(m) * dff;
+    for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+      Vec16<E> o;
+      const int t = c / T;
+      if (full_src != nullptr) {
+        load_vec(o, full_src + n * dff + c);
+      } else if (flags[slot0 + t]) {
+        load_vec(o, spill + n * dff + c);
+      } else {
+        const int64_t s = (slot0 + t) * C;
+        gather_tile_vec(o, vals + s, idx + s, cnt[slot0 + t], C, c - t * T);
+      }
+      store_vec(dst + c, o);
+    }
+  }
+  __syncthreads();  // every read of this row's slots is done before they are cleared
+  const int64_t nslots = static_cast<int64_t>(nt) * C;
+  for (int64_t i = threadIdx.x; i < nslots; i += kRowThreads) {
+    vals[slot0 * C + i] = E(0);
+    idx[slot0 * C + i] = 0;
+  }
+  for (int i = threadIdx.x; i < nt; i += kRowThreads) cnt[slot0 + i] = 0;
+}
+
+// One wave per (row, tile) of an existing h.
+template <typename E>
+__global__ __launch_bounds__(kRowThreads) void pack_tiles_kernel(
+    const E* __restrict__ h, int64_t pairs, int dff, int T, int C, int nt, E* __restrict__ vals,
+    uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt, uint8_t* __restrict__ flags) {
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kRowThreads / kWave);
+  for (int64_t q = static_cast<int64_t>(blockIdx.x) * (kRowThreads / kWave) + threadIdx.x / kWave;
+       q < pairs; q += waves) {
+    const int64_t n = q / nt;
+    const int t = static_cast<int>(q % nt);
+    pack_tile_from<E>(h + n * dff + static_cast<int64_t>(t) * T, T, C, vals + q * C, idx + q * C,
+                      cnt + q, flags + q, nullptr);
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(kRowThreads) void unpack_kernel(
+    int dff, int T, int C, int nt, const E* __restrict__ vals, const uint8_t* __restrict__ idx,
+    const uint8_t* __restrict__ cnt, const int32_t* __restrict__ dense_rows,
+    const E* __restrict__ dense_values, const int32_t* __restrict__ n_dense, int64_t cap,
+    E* __restrict__ h) {
+  constexpr int V = Vec16<E>::N;
+  __shared__ int found;
+  const int64_t n = blockIdx.x;
+  if (threadIdx.x == 0) {
+    // dense_rows[0 .. stored) is strictly ascending: binary search for n.
+    int64_t lo = 0, hi = min(static_cast<int64_t>(*n_dense), cap);
+    int res = -1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      const int64_t r = dense_rows[mid];
+      if (r == n) {
+        res = static_cast<int>(mid);
+        break;
+      }
+      if (r < n) lo = mid + 1; else hi = mid;
+    }
+    found = res;
+  }
+  __syncthreads();
+  const int m = found;
+  E* dst = h + n * dff;
+  if (m >= 0) {
+    const E* src = dense_values + static_cast<int64_t>(m) * dff;
+    for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+      Vec16<E> o;
+      load_vec(o, src + c);
+      store_vec(dst + c, o);
+    }
+    return;
+  }
+  const int64_t slot0 = n * nt;
+  for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+    const int t = c / T;
+    const int64_t s = (slot0 + t) * C;
+    Vec16<E> o;
+    gather_tile_vec(o, vals + s, idx + s, cnt[slot0 + t], C, c - t * T);
+    store_vec(dst + c, o);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_scan(const Geometry& g, const uint8_t* flags, int32_t* row_map,
+                             int32_t* dense_rows, int64_t dense_cap, int32_t* n_dense,
+                             int32_t* status, hipStream_t s) {
+  route_scan_kernel<<<1, kScanThreads, 0, s>>>(flags, g.n_rows, g.n_tiles, row_map, dense_rows,
+                                               dense_cap, n_dense, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* row_map,
+                              const uint8_t* flags, const void* spill, const void* full_src,
+                              void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
+                              int64_t dense_cap, hipStream_t s) {
+  if (g.n_rows == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(g.n_rows);
+  if (elem_bytes == 2) {
+    materialize_kernel<uint16_t><<<blocks, kRowThreads, 0, s>>>(
+        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
+        static_cast<const uint16_t*>(spill), static_cast<const uint16_t*>(full_src),
+        static_cast<uint16_t*>(vals), idx, cnt, static_cast<uint16_t*>(dense_values), dense_cap);
+  } else {
+    materialize_kernel<float><<<blocks, kRowThreads, 0, s>>>(
+        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags, static_cast<const float*>(spill),
+        static_cast<const float*>(full_src), static_cast<float*>(vals), idx, cnt,
+        static_cast<float*>(dense_values), dense_cap);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_tiles(const Geometry& g, const void* h, int elem_bytes, const PackOut& out,
+                             hipStream_t s) {
+  const int64_t pairs = g.n_rows * g.n_tiles;
+  if (pairs == 0) return hipSuccess;
+  const int64_t want = (pairs + 3) / 4;
+  const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
+  if (elem_bytes == 2) {
+    pack_tiles_kernel<uint16_t><<<blocks, kRowThreads, 0, s>>>(
+        static_cast<const uint16_t*>(h), pairs, g.d_ff, g.tile, g.capacity, g.n_tiles,
+        static_cast<uint16_t*>(out.vals), out.idx, out.cnt, out.flags);
+  } else {
+    pack_tiles_kernel<float><<<blocks, kRowThreads, 0, s>>>(
+        static_cast<const float*>(h), pairs, g.d_ff, g.tile, g.capacity, g.n_tiles,
+        static_cast<float*>(out.vals), out.idx, out.cnt, out.flags);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(const Geometry& g, int elem_bytes, const void* vals, const uint8_t* idx,
+                         const uint8_t* cnt, const int32_t* dense_rows, const void* dense_values,
+                         const int32_t* n_dense, int64_t dense_cap, void* h, hipStream_t s) {
+  if (g.n_rows == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(g.n_rows);
+  if (elem_bytes == 2) {
+    unpack_kernel<uint16_t><<<blocks, kRowThreads, 0, s>>>(
+        g.d_ff, g.tile, g.capacity, g.n_tiles, static_cast<const uint16_t*>(vals), idx, cnt,
+        dense_rows, static_cast<const uint16_t*>(dense_values), n_dense, dense_cap,
+        static_cast<uint16_t*>(h));
+  } else {
+    unpack_kernel<float><<<blocks, kRowThreads, 0, s>>>(
+        g.d_ff, g.tile, g.capacity, g.n_tiles, static_cast<const float*>(vals), idx, cnt,
+        dense_rows, static_cast<const float*>(dense_values), n_dense, dense_cap,
+        static_cast<float*>(h));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace twell

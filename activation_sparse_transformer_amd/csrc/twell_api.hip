@@ -1,0 +1,280 @@
+// The C ABI of libtwell.so (declared in include/twell.h): argument checks,
+// workspace carving and the launch sequence of each entry point.  All work
+// is enqueued on the caller's stream; nothing here synchronises the host.
+#include "../../include/twell.h"
+#include "kernels.h"
+
+#define TWELL_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace twell {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(int32_t dtype) { return dtype == TWELL_F32 ? 4 : 2; }
+
+// Geometry checks shared by every entry point.  `need_model` adds the
+// d_model requirements (not used by pack / unpack).
+int check_shape(const twell_shape* s, bool need_model) {
+  if (s == nullptr) return TWELL_ERR_INVALID_ARG;
+  if (s->n_rows < 0 || s->n_rows > INT32_MAX) return TWELL_ERR_INVALID_ARG;
+  if (s->dtype != TWELL_F32 && s->dtype != TWELL_BF16) return TWELL_ERR_INVALID_ARG;
+  if (s->reserved != 0) return TWELL_ERR_INVALID_ARG;
+  if (s->d_ff <= 0 || s->tile <= 0 || s->tile > 256 || s->d_ff % s->tile != 0)
+    return TWELL_ERR_INVALID_ARG;
+  if (s->capacity < 1 || s->capacity > s->tile || s->capacity > 255) return TWELL_ERR_INVALID_ARG;
+  if (need_model && (s->d_model <= 0 || s->d_model % 8 != 0)) return TWELL_ERR_INVALID_ARG;
+  if (s->tile != 64 && s->tile != 128 && s->tile != 256) return TWELL_ERR_UNSUPPORTED;
+  return TWELL_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_hybrid(const twell_hybrid* h, int64_t n_rows) {
+  if (h == nullptr || h->n_dense == nullptr || h->dense_capacity < 0) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(h->values) || !aligned16(h->indices) || !aligned16(h->counts) ||
+      !aligned16(h->dense_rows) || !aligned16(h->dense_values))
+    return TWELL_ERR_INVALID_ARG;
+  if (n_rows > 0 && (h->values == nullptr || h->indices == nullptr || h->counts == nullptr))
+    return TWELL_ERR_INVALID_ARG;
+  if (h->dense_capacity > 0 && (h->dense_rows == nullptr || h->dense_values == nullptr))
+    return TWELL_ERR_INVALID_ARG;
+  return TWELL_OK;
+}
+
+Geometry geometry(const twell_shape* s) {
+  Geometry g;
+  g.n_rows = s->n_rows;
+  g.d_model = s->d_model;
+  g.d_ff = s->d_ff;
+  g.tile = s->tile;
+  g.capacity = s->capacity;
+  g.n_tiles = s->d_ff / s->tile;
+  return g;
+}
+
+struct PackWorkspace {
+  uint8_t* flags;
+  int32_t* row_map;
+  void* spill;
+};
+
+size_t pack_ws_bytes(const twell_shape* s) {
+  const size_t n = static_cast<size_t>(s->n_rows);
+  return align_up(n * static_cast<size_t>(s->d_ff / s->tile)) + align_up(n * sizeof(int32_t));
+}
+
+size_t fwd_ws_bytes(const twell_shape* s) {
+  const size_t n = static_cast<size_t>(s->n_rows);
+  return pack_ws_bytes(s) + align_up(n * static_cast<size_t>(s->d_ff) * elem_bytes(s->dtype));
+}
+
+PackWorkspace carve(const twell_shape* s, void* ws, bool with_spill) {
+  PackWorkspace w;
+  const size_t n = static_cast<size_t>(s->n_rows);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  w.flags = p;
+  p += align_up(n * static_cast<size_t>(s->d_ff / s->tile));
+  w.row_map = reinterpret_cast<int32_t*>(p);
+  p += align_up(n * sizeof(int32_t));
+  w.spill = with_spill ? p : nullptr;
+  return w;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_ERR_HIP; }
+
+#define TWELL_TRY(expr)                          \
+  do {                                           \
+    const hipError_t e_ = (expr);                \
+    if (e_ != hipSuccess) return TWELL_ERR_HIP;  \
+  } while (0)
+
+// Steps 2-4 of the forward pass once the pack step has run: route, build
+// the dense rows, sparse product, dense fallback.
+int route_and_materialize(const Geometry& g, int eb, const PackWorkspace& w, const void* full_src,
+                          const twell_hybrid* hy, int32_t* d_status, hipStream_t st) {
+  TWELL_TRY(launch_route_scan(g, w.flags, w.row_map, hy->dense_rows, hy->dense_capacity,
+                              hy->n_dense, d_status, st));
+  TWELL_TRY(launch_materialize(g, eb, w.row_map, w.flags, w.spill, full_src, hy->values,
+                               hy->indices, hy->counts, hy->dense_values, hy->dense_capacity, st));
+  return TWELL_OK;
+}
+
+}  // namespace
+}  // namespace twell
+
+using namespace twell;
+
+TWELL_EXPORT int twell_version(void) { return TWELL_VERSION; }
+
+TWELL_EXPORT const char* twell_status_string(int status) {
+  switch (status) {
+    case TWELL_OK: return "ok";
+    case TWELL_ERR_INVALID_ARG: return "invalid argument";
+    case TWELL_ERR_UNSUPPORTED: return "unsupported geometry";
+    case TWELL_ERR_WORKSPACE: return "workspace too small";
+    case TWELL_ERR_HIP: return "HIP launch failed";
+    case TWELL_ERR_DENSE_CAPACITY: return "more dense rows than dense_capacity";
+    default: return "unknown status";
+  }
+}
+
+TWELL_EXPORT size_t ffn_sparse_workspace_size(const twell_shape* shape) {
+  if (check_shape(shape, true) != TWELL_OK) return 0;
+  return fwd_ws_bytes(shape);
+}
+
+TWELL_EXPORT size_t twell_pack_workspace_size(const twell_shape* shape) {
+  if (check_shape(shape, false) != TWELL_OK) return 0;
+  return pack_ws_bytes(shape);
+}
+
+namespace twell {
+namespace {
+
+// The forward pass; `ev`, when given, holds five events recorded on the
+// stream before step 1 and after each of steps 1-4.
+int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, const float* b_up,
+                 const void* w_down, void* y, const twell_hybrid* h_out, void* h_dense_debug,
+                 void* workspace, size_t workspace_bytes, int32_t* d_status, void* stream,
+                 void* const* ev) {
+  int rc = check_shape(shape, true);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_hybrid(h_out, g.n_rows)) != TWELL_OK) return rc;
+  if (g.n_rows > 0 && (x == nullptr || w_up_t == nullptr || b_up == nullptr || w_down == nullptr ||
+                       y == nullptr || workspace == nullptr))
+    return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_up_t) || !aligned16(w_down) || !aligned16(y) ||
+      !aligned16(h_dense_debug) || !aligned16(workspace))
+    return TWELL_ERR_INVALID_ARG;
+  if (ev != nullptr) {
+    for (int i = 0; i < 5; ++i)
+      if (ev[i] == nullptr) return TWELL_ERR_INVALID_ARG;
+  }
+  if (workspace_bytes < fwd_ws_bytes(shape)) return TWELL_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    return ev != nullptr ? hipEventRecord(static_cast<hipEvent_t>(ev[i]), st) : hipSuccess;
+  };
+  const int eb = elem_bytes(shape->dtype);
+  const PackWorkspace w = carve(shape, workspace, true);
+
+  TWELL_TRY(mark(0));
+  // 1. up-projection + bias + ReLU with the TwELL pack in its epilogue
+  PackOut po{h_out->values, h_out->indices, h_out->counts, w.flags, w.spill, h_dense_debug};
+  if (g.n_rows > 0) {
+    if (eb == 2)
+      TWELL_TRY(launch_up_pack_bf16(g, static_cast<const uint16_t*>(x),
+                                    static_cast<const uint16_t*>(w_up_t), b_up, po, st));
+    else
+      TWELL_TRY(launch_up_pack_f32(g, static_cast<const float*>(x),
+                                   static_cast<const float*>(w_up_t), b_up, po, st));
+  }
+  TWELL_TRY(mark(1));
+  // 2. route rows, build dense rows from the TwELL slots + spilled tiles
+  if ((rc = route_and_materialize(g, eb, w, nullptr, h_out, d_status, st)) != TWELL_OK) return rc;
+  TWELL_TRY(mark(2));
+  // 3. sparse down-projection of the TwELL rows
+  if (g.n_rows > 0)
+    TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts, w.row_map,
+                                 w_down, y, st));
+  TWELL_TRY(mark(3));
+  // 4. dense fallback for the dense rows
+  if (g.n_rows > 0) {
+    if (eb == 2)
+      TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(h_out->dense_values),
+                                     h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
+                                     static_cast<const uint16_t*>(w_down),
+                                     static_cast<uint16_t*>(y), st));
+    else
+      TWELL_TRY(launch_fallback_f32(g, static_cast<const float*>(h_out->dense_values),
+                                    h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
+                                    static_cast<const float*>(w_down), static_cast<float*>(y),
+                                    st));
+  }
+  TWELL_TRY(mark(4));
+  return TWELL_OK;
+}
+
+}  // namespace
+}  // namespace twell
+
+TWELL_EXPORT int ffn_sparse_forward(const twell_shape* shape, const void* x, const void* w_up_t,
+                                    const float* b_up, const void* w_down, void* y,
+                                    const twell_hybrid* h_out, void* h_dense_debug,
+                                    void* workspace, size_t workspace_bytes, int32_t* d_status,
+                                    void* stream) {
+  return forward_impl(shape, x, w_up_t, b_up, w_down, y, h_out, h_dense_debug, workspace,
+                      workspace_bytes, d_status, stream, nullptr);
+}
+
+TWELL_EXPORT int ffn_sparse_forward_events(const twell_shape* shape, const void* x,
+                                           const void* w_up_t, const float* b_up,
+                                           const void* w_down, void* y, const twell_hybrid* h_out,
+                                           void* h_dense_debug, void* workspace,
+                                           size_t workspace_bytes, int32_t* d_status, void* stream,
+                                           void* const* stage_events) {
+  if (stage_events == nullptr) return TWELL_ERR_INVALID_ARG;
+  return forward_impl(shape, x, w_up_t, b_up, w_down, y, h_out, h_dense_debug, workspace,
+                      workspace_bytes, d_status, stream, stage_events);
+}
+
+TWELL_EXPORT int twell_pack(const twell_shape* shape, const void* h, const twell_hybrid* out,
+                            void* workspace, size_t workspace_bytes, int32_t* d_status,
+                            void* stream) {
+  int rc = check_shape(shape, false);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_hybrid(out, g.n_rows)) != TWELL_OK) return rc;
+  if (g.n_rows > 0 && (h == nullptr || workspace == nullptr)) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(workspace)) return TWELL_ERR_INVALID_ARG;
+  if (workspace_bytes < pack_ws_bytes(shape)) return TWELL_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int eb = elem_bytes(shape->dtype);
+  const PackWorkspace w = carve(shape, workspace, false);
+  PackOut po{out->values, out->indices, out->counts, w.flags, nullptr, nullptr};
+  TWELL_TRY(launch_pack_tiles(g, h, eb, po, st));
+  return route_and_materialize(g, eb, w, h, out, d_status, st);
+}
+
+TWELL_EXPORT int twell_unpack(const twell_shape* shape, const twell_hybrid* in, void* h,
+                              void* stream) {
+  int rc = check_shape(shape, false);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_hybrid(in, g.n_rows)) != TWELL_OK) return rc;
+  if (g.n_rows > 0 && h == nullptr) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(h)) return TWELL_ERR_INVALID_ARG;
+  return hip_status(launch_unpack(g, elem_bytes(shape->dtype), in->values, in->indices, in->counts,
+                                  in->dense_rows, in->dense_values, in->n_dense,
+                                  in->dense_capacity, h, static_cast<hipStream_t>(stream)));
+}
+
+TWELL_EXPORT int twell_spmm(const twell_shape* shape, const twell_hybrid* in, const void* w_down,
+                            void* y, void* stream) {
+  int rc = check_shape(shape, true);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_hybrid(in, g.n_rows)) != TWELL_OK) return rc;
+  if (g.n_rows > 0 && (w_down == nullptr || y == nullptr)) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(w_down) || !aligned16(y)) return TWELL_ERR_INVALID_ARG;
+  if (g.n_rows == 0) return TWELL_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int eb = elem_bytes(shape->dtype);
+  // every row from its TwELL slots (dense rows hold none and come out 0) ...
+  TWELL_TRY(launch_spmm_sparse(g, eb, in->values, in->indices, in->counts, nullptr, w_down, y, st));
+  // ... then the stored dense rows are overwritten by the fallback GEMM
+  if (eb == 2)
+    TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(in->dense_values),
+                                   in->dense_rows, in->n_dense, in->dense_capacity,
+                                   static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y),
+                                   st));
+  else
+    TWELL_TRY(launch_fallback_f32(g, static_cast<const float*>(in->dense_values), in->dense_rows,
+                                  in->n_dense, in->dense_capacity,
+                                  static_cast<const float*>(w_down), static_cast<float*>(y), st));
+  return TWELL_OK;
+}

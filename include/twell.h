@@ -1,0 +1,196 @@
+/*
+ * twell.h - C ABI of libtwell.so: the forward pass of a ReLU-activation-sparse
+ * transformer feed-forward layer whose hidden activations are stored in the
+ * hybrid Tile-wise ELLPACK (TwELL) format, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages on "Sparser, Faster, Lighter Transformer Language Models",
+ * Sakana AI + NVIDIA):
+ *  - "Sparser, Faster, Lighter Transformer Language Models (Sakana AI +
+ *    NVIDIA)" (wiki note), Figure 1 description and packing-format flowchart:
+ *    TwELL keeps, per column tile of width T (tile index t), a values array of
+ *    the non-zeros only, their tile-local indices and a per-tile non-zero
+ *    count; the hybrid variant splits token rows between TwELL and a dense
+ *    matrix according to how their non-zeros distribute.
+ *  - "Nvidia and Sakana make LLMs 30% faster by doing less math", section
+ *    "Reshaping math for the GPU": sparse tokens take the fast path, the rare
+ *    dense tokens go to a dense matrix ("safety valve").
+ *  - "SakanaAI/sparser-faster-llms: How TwELL Makes Sparse Transformers Run
+ *    Like They Were Built for Hopper", section "TwELL: The Packing Format That
+ *    Fits the Machine": dense-to-TwELL, TwELL-to-dense and fused MLP execution.
+ *  - "The Relentless Search for Efficiency in Large-Scale Language Models",
+ *    section "The Challenge of Sparsity Ignored by GPUs": a hidden unit is
+ *    active when it is non-zero after the ReLU.
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers on the current HIP device,
+ *    16-byte aligned, owned by the caller.  The library never allocates or
+ *    frees memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on that stream and returns; nothing is
+ *    synchronised on the host.  Outputs are valid once the stream reaches the
+ *    enqueued work.  Calls are thread-safe; calls that share output or
+ *    workspace buffers must be ordered by the caller.
+ *  - Return value: TWELL_OK (0) or a negative twell_status.  Argument errors
+ *    are detected on the host before anything is enqueued.  Conditions only
+ *    known on the device are reported through the optional device word
+ *    `d_status` (see TWELL_ERR_DENSE_CAPACITY).
+ *  - Element type: `dtype` = TWELL_F32 (IEEE float) or TWELL_BF16 (bfloat16
+ *    bits).  x, the weights, y, TwELL values and dense rows all use it; the
+ *    up-projection bias is always float32; accumulation is always float32;
+ *    results are rounded to the storage type round-to-nearest-even.
+ *
+ * Layouts (row-major, C order; nt = d_ff / tile)
+ *  - x       [n_rows][d_model]
+ *  - w_up_t  [d_ff][d_model]  W_up stored transposed (one row per neuron)
+ *  - b_up    [d_ff] float32
+ *  - w_down  [d_ff][d_model]  one row of W_down per neuron
+ *  - y, h    [n_rows][d_model] / [n_rows][d_ff]
+ *  - TwELL   values [n_rows][nt][capacity], indices [n_rows][nt][capacity]
+ *            uint8, counts [n_rows][nt] uint8
+ *
+ * Format rules (readings of the pages where they are silent)
+ *  - Tile t of a row is columns [t*tile, (t+1)*tile).  Inside a tile the
+ *    non-zeros are kept in ascending column order; slot k holds the k-th.
+ *  - A value is non-zero when it is != 0 in the storage type (-0.0 is zero,
+ *    NaN is non-zero).  The ReLU writes +0.0 for inactive units.
+ *  - A tile overflows when its count exceeds `capacity`.  One overflowing
+ *    tile makes the whole token row dense: its counts are 0, all its slots
+ *    are padding, and its full row is stored in dense_values.  Dense rows are
+ *    listed in ascending token order.
+ *  - Padding slots hold value +0.0 (all-zero bits) and index 0.
+ */
+#ifndef TWELL_H
+#define TWELL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TWELL_VERSION 1
+
+typedef enum twell_status {
+  TWELL_OK = 0,
+  TWELL_ERR_INVALID_ARG = -1,    /* null pointer, negative size, bad geometry */
+  TWELL_ERR_UNSUPPORTED = -2,    /* valid TwELL geometry this build has no kernel for */
+  TWELL_ERR_WORKSPACE = -3,      /* workspace smaller than the *_workspace_size query */
+  TWELL_ERR_HIP = -4,            /* a HIP launch failed */
+  TWELL_ERR_DENSE_CAPACITY = -5  /* device-side: more dense rows than dense_capacity */
+} twell_status;
+
+typedef enum twell_dtype { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
+
+/* Shape of one FFN layer and its TwELL geometry.
+ * Requirements: n_rows >= 0 and < 2^31; d_model > 0 and a multiple of 8;
+ * d_ff > 0 and a multiple of tile; tile in {64, 128, 256} (other tile widths
+ * are TWELL_ERR_UNSUPPORTED); 1 <= capacity <= min(tile, 255); dtype a
+ * twell_dtype.  d_model is ignored by twell_pack and twell_unpack. */
+typedef struct twell_shape {
+  int64_t n_rows;   /* N, tokens */
+  int32_t d_model;  /* model width */
+  int32_t d_ff;     /* hidden width */
+  int32_t tile;     /* T, tile width */
+  int32_t capacity; /* C, slots per tile */
+  int32_t dtype;    /* twell_dtype */
+  int32_t reserved; /* must be 0 */
+} twell_shape;
+
+/* A hybrid TwELL matrix [n_rows][d_ff] (all device pointers, caller-owned).
+ *  values       [n_rows][nt][capacity]   dtype
+ *  indices      [n_rows][nt][capacity]   uint8, tile-local column
+ *  counts       [n_rows][nt]             uint8
+ *  dense_rows   [dense_capacity]         int32, ascending token rows
+ *  dense_values [dense_capacity][d_ff]   dtype, the dense rows bit for bit
+ *  n_dense      device int32: number of dense rows (may exceed
+ *               dense_capacity after a TWELL_ERR_DENSE_CAPACITY pack; only
+ *               the first dense_capacity are stored)
+ * dense_rows / dense_values may be NULL when dense_capacity == 0. */
+typedef struct twell_hybrid {
+  void* values;
+  uint8_t* indices;
+  uint8_t* counts;
+  int32_t* dense_rows;
+  void* dense_values;
+  int32_t* n_dense;
+  int64_t dense_capacity;
+} twell_hybrid;
+
+/* Library version (TWELL_VERSION). */
+int twell_version(void);
+
+/* Static string naming a twell_status value ("unknown status" otherwise). */
+const char* twell_status_string(int status);
+
+/* Bytes of device workspace ffn_sparse_forward needs for this shape
+ * (0 for an invalid shape).  Sized for the worst case: every tile spilled. */
+size_t ffn_sparse_workspace_size(const twell_shape* shape);
+
+/* The fused forward pass: y = ReLU(x W_up + b_up) W_down, with the hidden
+ * activations h produced directly in hybrid TwELL form.
+ *   1. up-projection GEMM (MFMA for bf16) + bias + ReLU + rounding, whose
+ *      epilogue packs each (row, tile) of h into TwELL and flags overflow;
+ *   2. row routing: a row with an overflowing tile is dense; dense rows are
+ *      numbered in ascending order and copied to dense_values, their TwELL
+ *      slots cleared;
+ *   3. sparse down-projection of the TwELL rows: y[n] = sum over stored slots
+ *      of value * w_down[t*tile + index];
+ *   4. dense fallback GEMM for the dense rows: y[dense_rows[m]] =
+ *      dense_values[m] W_down.
+ * Arguments: shape (host pointer); x, w_up_t, b_up, w_down inputs; y output;
+ * h_out (host pointer to a struct of device pointers) receives h in hybrid
+ * TwELL form; h_dense_debug, if non-NULL, receives h [n_rows][d_ff] exactly
+ * as packed (for bit-exact checks; costs one extra write of h); workspace /
+ * workspace_bytes: scratch of at least ffn_sparse_workspace_size(shape)
+ * bytes, contents undefined on entry and exit; d_status, if non-NULL, is set
+ * on the device to TWELL_OK or TWELL_ERR_DENSE_CAPACITY.  On
+ * TWELL_ERR_DENSE_CAPACITY the rows past dense_capacity are neither stored
+ * nor computed, so y is undefined for them; *n_dense holds the true count so
+ * the caller can retry with a larger dense buffer.  n_rows == 0 only sets
+ * *n_dense = 0 and *d_status = TWELL_OK. */
+int ffn_sparse_forward(const twell_shape* shape, const void* x, const void* w_up_t,
+                       const float* b_up, const void* w_down, void* y,
+                       const twell_hybrid* h_out, void* h_dense_debug, void* workspace,
+                       size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/* ffn_sparse_forward that also records five caller-created HIP events
+ * (stage_events[0..4], hipEvent_t passed as void*) on `stream`: before step
+ * 1 and after each of steps 1-4, so a caller can time every stage with
+ * hipEventElapsedTime on the stream the kernels run on.  Same arguments,
+ * results and errors as ffn_sparse_forward; a NULL array or event is
+ * TWELL_ERR_INVALID_ARG. */
+int ffn_sparse_forward_events(const twell_shape* shape, const void* x, const void* w_up_t,
+                              const float* b_up, const void* w_down, void* y,
+                              const twell_hybrid* h_out, void* h_dense_debug, void* workspace,
+                              size_t workspace_bytes, int32_t* d_status, void* stream,
+                              void* const* stage_events);
+
+/* Bytes of device workspace twell_pack needs (0 for an invalid shape). */
+size_t twell_pack_workspace_size(const twell_shape* shape);
+
+/* dense_to_twell: pack h [n_rows][d_ff] into the hybrid `out` under the
+ * format rules above (same rules and same result as step 1-2 of
+ * ffn_sparse_forward applied to h).  Dense rows are copied bit for bit; in
+ * sparse rows a -0.0 is dropped like +0.0.  workspace / d_status as for
+ * ffn_sparse_forward. */
+int twell_pack(const twell_shape* shape, const void* h, const twell_hybrid* out,
+               void* workspace, size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/* twell_to_dense: h [n_rows][d_ff] = +0.0 everywhere, then every stored slot
+ * (k < counts) is written to its column and every stored dense row
+ * (the first min(*n_dense, dense_capacity) entries) is copied to its row.
+ * dense_rows must be strictly ascending. */
+int twell_unpack(const twell_shape* shape, const twell_hybrid* in, void* h, void* stream);
+
+/* The hybrid down-projection y [n_rows][d_model] = unpack(in) W_down:
+ * TwELL rows by the sparse gather kernel, stored dense rows by the dense
+ * fallback GEMM (float32 accumulation, one rounding at the end). */
+int twell_spmm(const twell_shape* shape, const twell_hybrid* in, const void* w_down, void* y,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H */

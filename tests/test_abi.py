@@ -1,0 +1,119 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and answers the host-only calls (version, status strings,
+workspace sizes, argument validation) without touching a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from activation_sparse_transformer_amd import twell
+
+# Tests that hand the library fake (never dereferenced) device addresses run
+# only where no GPU could execute a kernel, should a host check ever miss.
+no_gpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                                 reason="fake device pointers are passed only on a GPU-less host")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twell.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(twell.LIB_PATH):
+        pytest.fail("libtwell.so is not built: run python -m activation_sparse_transformer_amd.build")
+    return twell.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert set(names) == set(twell.EXPORTS), names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", twell.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing else of the library's own leaks out of the ABI
+    ours = {n for n in exported if n.startswith(("twell", "ffn_"))}
+    assert ours == set(twell.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.twell_version() == 1
+    assert twell.status_string(0) == "ok"
+    assert "dense_capacity" in twell.status_string(twell.TWELL_ERR_DENSE_CAPACITY)
+    assert twell.status_string(12345) == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    s = twell.make_shape(4096, 2048, 8192, 128, 4, __import__("torch").bfloat16)
+    ws = twell.ffn_workspace_bytes(s)
+    # flags [N, nt] + row map [N] int32 + spill [N, d_ff] bf16, each 256-aligned
+    assert ws == 4096 * 64 + 4096 * 4 + 4096 * 8192 * 2
+    assert twell.pack_workspace_bytes(s) == 4096 * 64 + 4096 * 4
+    bad = twell.make_shape(16, 2048, 8192, 100, 4, __import__("torch").bfloat16)
+    assert twell.ffn_workspace_bytes(bad) == 0
+
+
+def _call_forward(lib, shape, hybrid):
+    return lib.ffn_sparse_forward(ctypes.byref(shape), None, None, None, None, None,
+                                  ctypes.byref(hybrid) if hybrid is not None else None,
+                                  None, None, 0, None, None)
+
+
+@no_gpu_only
+@pytest.mark.parametrize("field,value,code", [
+    ("tile", 100, twell.TWELL_ERR_INVALID_ARG),      # does not divide d_ff
+    ("tile", 32, twell.TWELL_ERR_UNSUPPORTED),       # valid geometry, no kernel
+    ("capacity", 0, twell.TWELL_ERR_INVALID_ARG),
+    ("capacity", 129, twell.TWELL_ERR_INVALID_ARG),  # > T
+    ("d_model", 12, twell.TWELL_ERR_INVALID_ARG),    # not a multiple of 8
+    ("n_rows", -1, twell.TWELL_ERR_INVALID_ARG),
+    ("dtype", 7, twell.TWELL_ERR_INVALID_ARG),
+    ("reserved", 1, twell.TWELL_ERR_INVALID_ARG),
+])
+def test_shape_validation(lib, field, value, code):
+    s = twell.Shape(64, 128, 512, 128, 4, 1, 0)
+    setattr(s, field, value)
+    h = twell.HybridStruct(1, 1, 1, None, None, 1, 0)
+    assert _call_forward(lib, s, h) == code
+
+
+@no_gpu_only
+def test_null_arguments_rejected_on_host(lib):
+    s = twell.Shape(64, 128, 512, 128, 4, 1, 0)
+    assert _call_forward(lib, s, None) == twell.TWELL_ERR_INVALID_ARG
+    h = twell.HybridStruct(1, 1, 1, None, None, 1, 0)
+    assert _call_forward(lib, s, h) == twell.TWELL_ERR_INVALID_ARG  # x etc. are NULL
+    h_nodense = twell.HybridStruct(1, 1, 1, None, None, 1, 5)  # capacity 5, no buffers
+    assert lib.twell_unpack(ctypes.byref(s), ctypes.byref(h_nodense), 1, None) == \
+        twell.TWELL_ERR_INVALID_ARG
+    assert lib.twell_spmm(None, ctypes.byref(h), 1, 1, None) == twell.TWELL_ERR_INVALID_ARG
+
+
+@no_gpu_only
+def test_workspace_too_small_rejected_on_host(lib):
+    s = twell.Shape(64, 128, 512, 128, 4, 1, 0)
+    a = 4096  # a well-aligned address that the host-side checks never dereference
+    h = twell.HybridStruct(a, a, a, None, None, a, 0)
+    rc = lib.ffn_sparse_forward(ctypes.byref(s), a, a, a, a, a, ctypes.byref(h), None, a, 16,
+                                None, None)
+    assert rc == twell.TWELL_ERR_WORKSPACE
+    rc = lib.twell_pack(ctypes.byref(s), a, ctypes.byref(h), a, 16, None, None)
+    assert rc == twell.TWELL_ERR_WORKSPACE
+    # a misaligned pointer is rejected before the size check
+    rc = lib.twell_pack(ctypes.byref(s), a + 2, ctypes.byref(h), a, 1 << 30, None, None)
+    assert rc == twell.TWELL_ERR_INVALID_ARG

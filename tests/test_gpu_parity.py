@@ -1,0 +1,222 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle, at sizes the
+oracle finishes in seconds that still span several tiles and ragged tails.
+
+Bars: TwELL packing bit-exact (indices, counts, values as bit patterns, dense
+row list, dense rows); y and h within max|err| <= tol * max|ref| with tol =
+1e-4 (float32) / 1e-2 (bfloat16); integer-valued products exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_transformer_amd import twell
+from activation_sparse_transformer_amd.synth import CONFIGS, make_inputs
+from gpu_helpers import (TOL, as_f32, as_f64, assert_close_rel, assert_pack_matches,
+                         inputs_to_device, oracle_inputs, say, u32)
+
+pytestmark = pytest.mark.gpu
+DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def sparse_h(seed, n, dff, density, dtype, negzero=False, nan=False):
+    rng = np.random.default_rng(seed)
+    h = np.abs(rng.standard_normal((n, dff))).astype(np.float32) + 0.01
+    h *= np.where(rng.random((n, dff)) < 0.5, 1, -1).astype(np.float32)
+    h[rng.random((n, dff)) >= density] = 0.0
+    if negzero:
+        h[(h == 0) & (rng.random((n, dff)) < 0.3)] = -0.0
+    if nan and n:
+        h[rng.integers(0, n, 3), rng.integers(0, dff, 3)] = np.nan
+    t = torch.from_numpy(h).to(dtype)
+    return t, as_f32(t)  # GPU input and its exact float32 value on the host
+
+
+# ---------------------------------------------------------------- pack / unpack
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("T,C,density", [(64, 8, 0.08), (128, 4, 0.02), (256, 8, 0.03), (128, 1, 0.005)])
+@pytest.mark.parametrize("n", [1, 77, 300])
+def test_pack_unpack_bitexact(dtype, T, C, density, n):
+    say(f"pack/unpack {dtype} T={T} C={C} n={n}")
+    dff = T * 5
+    ht, hh = sparse_h(1000 + T + C + n, n, dff, density, DT[dtype], negzero=True, nan=(n == 300))
+    hy, status = twell.twell_pack(ht.cuda(), T, C)
+    torch.cuda.synchronize()
+    assert int(status.item()) == twell.TWELL_OK
+    ref = assert_pack_matches(hy, hh)
+    u = twell.twell_unpack(hy)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(u32(as_f32(u)), u32(oracle.unpack(ref)))
+
+
+def test_pack_all_zero_and_all_dense():
+    for fill, dense in ((0.0, False), (1.5, True)):
+        h = torch.full((40, 512), fill, dtype=torch.bfloat16, device="cuda")
+        hy, status = twell.twell_pack(h, 128, 4)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        assert hy.n_dense_host() == (40 if dense else 0)
+        assert_pack_matches(hy, as_f32(h))
+
+
+def test_pack_dense_capacity_exceeded():
+    ht, hh = sparse_h(5, 200, 512, 0.06, torch.bfloat16)
+    ref = oracle.pack(hh, 128, 4)
+    assert ref.n_dense > 10
+    hy, status = twell.twell_pack(ht.cuda(), 128, 4, dense_capacity=10)
+    torch.cuda.synchronize()
+    assert int(status.item()) == twell.TWELL_ERR_DENSE_CAPACITY
+    assert hy.n_dense_host() == ref.n_dense
+    np.testing.assert_array_equal(hy.dense_rows.cpu().numpy(), ref.dense_rows[:10])
+    np.testing.assert_array_equal(u32(as_f32(hy.dense_values)), u32(ref.dense_values[:10]))
+    # every dense row, stored or not, has cleared TwELL slots
+    np.testing.assert_array_equal(hy.counts.cpu().numpy(), ref.counts)
+    np.testing.assert_array_equal(u32(as_f32(hy.values)), u32(ref.values))
+
+
+def test_pack_zero_rows():
+    h = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    hy, status = twell.twell_pack(h, 128, 4)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and hy.n_dense_host() == 0
+    assert twell.twell_unpack(hy).shape == (0, 256)
+
+
+# ------------------------------------------------------------------------ spmm
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("n,dm,T,C", [(50, 136, 64, 4), (300, 520, 128, 4), (130, 64, 256, 8)])
+def test_spmm_integer_exact(dtype, n, dm, T, C):
+    say(f"spmm integer {dtype} n={n} dm={dm} T={T}")
+    rng = np.random.default_rng(n + dm)
+    dff = 3 * T
+    h = rng.integers(-2, 3, size=(n, dff)).astype(np.float32)
+    h[rng.random((n, dff)) < 0.96] = 0
+    w = rng.integers(-1, 2, size=(dff, dm)).astype(np.float32)
+    w[rng.random((dff, dm)) < 0.7] = 0
+    hy, _ = twell.twell_pack(torch.from_numpy(h).to(DT[dtype]).cuda(), T, C)
+    y = twell.twell_spmm(hy, torch.from_numpy(w).to(DT[dtype]).cuda())
+    torch.cuda.synchronize()
+    ref_h = assert_pack_matches(hy, h)
+    assert ref_h.n_dense > 0 and ref_h.n_dense < n
+    y_ref = oracle.spmm(ref_h, w.astype(np.float64))
+    assert np.max(np.abs(y_ref)) <= 256  # every value and partial sum is exact in bf16 / fp32
+    np.testing.assert_array_equal(as_f64(y), y_ref)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_spmm_identity_is_unpack(dtype):
+    ht, hh = sparse_h(9, 90, 256, 0.05, DT[dtype])
+    hy, _ = twell.twell_pack(ht.cuda(), 64, 4)
+    eye = torch.eye(256, dtype=DT[dtype], device="cuda")
+    y = twell.twell_spmm(hy, eye)
+    u = twell.twell_unpack(hy)
+    torch.cuda.synchronize()
+    assert hy.n_dense_host() > 0
+    np.testing.assert_array_equal(u32(as_f32(y)), u32(as_f32(u)))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_spmm_random_within_tolerance(dtype):
+    ht, hh = sparse_h(11, 257, 640, 0.03, DT[dtype])
+    rng = np.random.default_rng(2)
+    w = torch.from_numpy(rng.standard_normal((640, 328)).astype(np.float32)).to(DT[dtype])
+    hy, _ = twell.twell_pack(ht.cuda(), 128, 4)
+    y = twell.twell_spmm(hy, w.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.spmm(oracle.pack(hh, 128, 4), as_f64(w))
+    assert_close_rel(as_f64(y), ref, TOL[DT[dtype]])
+
+
+# --------------------------------------------------------------------- forward
+SMALL = [
+    # (config, n_rows, d_model, d_ff): ragged N, K tails, partial column blocks
+    ("tiny_fp32", 64, 128, 512),
+    ("tiny_fp32", 45, 72, 320),
+    ("ffn_1b_bf16", 300, 200, 640),
+    ("ffn_1b_bf16", 37, 256, 384),
+    ("ffn_1b_bf16", 1, 64, 128),
+    ("hybrid_stress_bf16", 260, 264, 1152),
+    ("decode_bf16", 16, 512, 1024),
+    ("large_bf16", 129, 136, 768),
+]
+
+
+def run_forward(cfg, t, debug=True, dense_capacity=None):
+    d = inputs_to_device(t)
+    out = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
+                                   cfg.capacity, dense_capacity=dense_capacity, debug_h=debug)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,n,dm,dff", SMALL)
+def test_forward_small(name, n, dm, dff):
+    cfg = CONFIGS[name].replace(n_rows=n, d_model=dm, d_ff=dff)
+    say(f"forward {name} n={n} dm={dm} dff={dff}")
+    t = make_inputs(cfg)
+    out = run_forward(cfg, t)
+    assert int(out.status.item()) == twell.TWELL_OK
+    h_ref, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    tol = TOL[cfg.torch_dtype]
+    assert_close_rel(as_f64(out.h_debug), h_ref, tol, "h")
+    ref = assert_pack_matches(out.hybrid, as_f32(out.h_debug))
+    assert_close_rel(as_f64(out.y), y_ref, tol, "y")
+    say(f"  n_dense={ref.n_dense}")
+    # the debug store changes nothing, and the pass is deterministic
+    out2 = run_forward(cfg, t, debug=False)
+    np.testing.assert_array_equal(u32(as_f32(out2.y)), u32(as_f32(out.y)))
+    np.testing.assert_array_equal(out2.hybrid.counts.cpu().numpy(), out.hybrid.counts.cpu().numpy())
+    np.testing.assert_array_equal(u32(as_f32(out2.hybrid.values)), u32(as_f32(out.hybrid.values)))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_forward_bias_limits(dtype):
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=150, d_model=128, d_ff=512, dtype=dtype)
+    t = make_inputs(cfg)
+    t["b_up"] = torch.full_like(t["b_up"], -1e4)
+    out = run_forward(cfg, t)
+    assert out.hybrid.n_dense_host() == 0
+    assert torch.all(out.hybrid.counts == 0)
+    assert torch.all(out.y.view(torch.int16 if dtype == "bf16" else torch.int32) == 0)  # +0 bits
+    t["b_up"] = torch.full_like(t["b_up"], 1e4)
+    out = run_forward(cfg, t)
+    assert out.hybrid.n_dense_host() == 150  # every tile is full, every row dense
+    _, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    assert_close_rel(as_f64(out.y), y_ref, TOL[cfg.torch_dtype])
+
+
+def test_forward_dense_capacity_exceeded():
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=200, d_model=128, d_ff=1024)
+    t = make_inputs(cfg)
+    out = run_forward(cfg, t, dense_capacity=3)
+    h_ref = oracle.pack(as_f32(out.h_debug), cfg.tile, cfg.capacity)
+    assert h_ref.n_dense > 3
+    assert int(out.status.item()) == twell.TWELL_ERR_DENSE_CAPACITY
+    assert out.hybrid.n_dense_host() == h_ref.n_dense
+    np.testing.assert_array_equal(out.hybrid.dense_rows.cpu().numpy(), h_ref.dense_rows[:3])
+
+
+def test_forward_zero_rows():
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=0, d_model=128, d_ff=512)
+    t = make_inputs(cfg)
+    out = run_forward(cfg, t)
+    assert int(out.status.item()) == 0 and out.hybrid.n_dense_host() == 0
+    assert out.y.shape == (0, 128)
+
+
+def test_forward_matches_standalone_pack_and_spmm():
+    """The fused path equals pack(h) followed by spmm, bit for bit."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=333, d_model=256, d_ff=1024)
+    t = make_inputs(cfg)
+    out = run_forward(cfg, t)
+    hy, _ = twell.twell_pack(out.h_debug, cfg.tile, cfg.capacity)
+    y2 = twell.twell_spmm(hy, t["w_down"].cuda())
+    torch.cuda.synchronize()
+    for a, b in ((out.hybrid.counts, hy.counts), (out.hybrid.indices, hy.indices)):
+        np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
+    np.testing.assert_array_equal(u32(as_f32(out.hybrid.values)), u32(as_f32(hy.values)))
+    nd = hy.n_dense_host()
+    assert nd == out.hybrid.n_dense_host() and nd > 0
+    np.testing.assert_array_equal(u32(as_f32(out.hybrid.dense_values[:nd])),
+                                  u32(as_f32(hy.dense_values[:nd])))
+    np.testing.assert_array_equal(u32(as_f32(out.y)), u32(as_f32(y2)))
