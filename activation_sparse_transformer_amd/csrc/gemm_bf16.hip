@@ -202,57 +202,339 @@ __device__ __forceinline__ void mfma_mainloop(
   }
 }
 
+// ============================================================ fast path
+// For K a multiple of 64.  Both operand tiles live in LDS as rows of 64
+// K-elements (128 B) without padding; the 16-byte chunk kc of row r sits at
+// chunk position kc ^ swz(r), so the 16 rows read by one MFMA fragment load
+// fall on distinct banks.  A K-major operand is copied global -> LDS by
+// global_load_lds_dwordx4 (no VGPR staging): one instruction of a wave fills
+// one 1 KB block = 8 rows, and lane l fetches the global chunk that belongs at
+// LDS position l.  A [K][N] operand (w_down) goes through registers and is
+// transposed 4x8 on the way into LDS.  Two LDS stages, 8 waves (2 per SIMD),
+// one barrier per 64-wide K step.
+namespace fast {
+
+constexpr int BKF = 64;
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+// element offset of (row r, 16-byte chunk kc) inside a swizzled operand tile
+__device__ __forceinline__ int tofs(int r, int kc) { return r * BKF + ((kc ^ swz(r)) << 3); }
+
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NW = WAVES_M * WAVES_N;
+  static constexpr int NT = NW * kWave;
+  static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+  static constexpr int FM = WTM / 16, FN = WTN / 16;
+  static constexpr int A_ISSUE = BM / (8 * NW);  // DMA instructions per thread per stage
+  static constexpr int B_ISSUE = BN / (8 * NW);
+  static constexpr int BT_ITEMS = ((BN / 8) * (BKF / 4) + NT - 1) / NT;  // 4x8 blocks per thread
+  static constexpr int STAGE = (BM + BN) * BKF;                // elements per LDS stage
+  static_assert(A_ISSUE * 8 * NW == BM && B_ISSUE * 8 * NW == BN, "whole 1 KB blocks per wave");
+  static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "16x16 blocks");
+};
+
+// Global source of the chunk each lane fetches for DMA instruction i of a
+// K-major operand (rows r0.., clamped to nrows-1: rows past the end feed only
+// outputs that are never stored).
+template <int ISSUE, int NW>
+__device__ __forceinline__ void dma_sources(const uint16_t* __restrict__ base, int64_t ld, int nrows,
+                                            int r0, const uint16_t* (&src)[ISSUE]) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < ISSUE; ++i) {
+    const int blk = wave + NW * i;
+    const int r = blk * 8 + lane / 8;
+    const int kc = (lane & 7) ^ swz(r);
+    const int gr = min(r0 + r, nrows - 1);
+    src[i] = base + static_cast<int64_t>(gr) * ld + kc * 8;
+  }
+}
+
+template <int ISSUE, int NW>
+__device__ __forceinline__ void dma_issue(const uint16_t* const* src, int k0, uint16_t* tile) {
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < ISSUE; ++i)
+    __builtin_amdgcn_global_load_lds(src[i] + k0, tile + (wave + NW * i) * 512, 16, 0, 0);
+}
+
+// [K][N] operand: item (nv, kq) = rows k0+4kq..+3, columns n0+8nv..+7.
+template <class CF>
+__device__ __forceinline__ void bt_load(const uint16_t* __restrict__ B, int64_t ldb, int N, int n0,
+                                        int k0, uint4 (&reg)[CF::BT_ITEMS][4]) {
+  static_assert(CF::BT_ITEMS * CF::NT == (CF::BN / 8) * (BKF / 4), "transposed B splits evenly");
+#pragma unroll
+  for (int it = 0; it < CF::BT_ITEMS; ++it) {
+    const int item = threadIdx.x + it * CF::NT;
+    const int nv = item % (CF::BN / 8), kq = item / (CF::BN / 8);
+    const int gn = min(n0 + nv * 8, N - 8);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      reg[it][r] = *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(k0 + kq * 4 + r) * ldb + gn);
+  }
+}
+
+template <class CF>
+__device__ __forceinline__ void bt_store(uint16_t* __restrict__ tile, const uint4 (&reg)[CF::BT_ITEMS][4]) {
+#pragma unroll
+  for (int it = 0; it < CF::BT_ITEMS; ++it) {
+    const int item = threadIdx.x + it * CF::NT;
+    const int nv = item % (CF::BN / 8), kq = item / (CF::BN / 8);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      uint32_t d[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) d[r] = pick(reg[it][r], n / 2);
+      const uint32_t lo = (n & 1) ? ((d[0] >> 16) | (d[1] & 0xffff0000u)) : ((d[0] & 0xffffu) | (d[1] << 16));
+      const uint32_t hi = (n & 1) ? ((d[2] >> 16) | (d[3] & 0xffff0000u)) : ((d[2] & 0xffffu) | (d[3] << 16));
+      const int row = nv * 8 + n;
+      *reinterpret_cast<uint2*>(tile + tofs(row, kq >> 1) + (kq & 1) * 4) = make_uint2(lo, hi);
+    }
+  }
+}
+
+template <class CF>
+__device__ __forceinline__ void compute_stage(const uint16_t* __restrict__ sA,
+                                              const uint16_t* __restrict__ sB,
+                                              f32x4_t (&acc)[CF::FM][CF::FN]) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+#pragma unroll
+  for (int ks = 0; ks < BKF / 32; ++ks) {
+    const int kc = ks * 4 + (lane >> 4);
+    bf16x8_t a[CF::FM], b[CF::FN];
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t*>(sA + tofs(wm * CF::WTM + i * 16 + (lane & 15), kc));
+#pragma unroll
+    for (int j = 0; j < CF::FN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8_t*>(sB + tofs(wn * CF::WTN + j * 16 + (lane & 15), kc));
+#pragma unroll
+    for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// C[BM x BN] = A[m0.., :] B^T with A [M][K] K-major and B either [N][K]
+// (B_NK) or [K][N].  K % 64 == 0.  `lds` holds two stages.
+template <class CF, bool B_NK>
+__device__ __forceinline__ void mainloop(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
+                                         const uint16_t* __restrict__ B, int64_t ldb, int N, int n0,
+                                         int K, uint16_t* lds, f32x4_t (&acc)[CF::FM][CF::FN]) {
+#pragma unroll
+  for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* asrc[CF::A_ISSUE];
+  dma_sources<CF::A_ISSUE, CF::NW>(A, lda, M, m0, asrc);
+  const uint16_t* bsrc[B_NK ? CF::B_ISSUE : 1];
+  uint4 breg[B_NK ? 1 : CF::BT_ITEMS][4];
+  if constexpr (B_NK) dma_sources<CF::B_ISSUE, CF::NW>(B, ldb, N, n0, bsrc);
+
+  const int KT = K / BKF;
+  dma_issue<CF::A_ISSUE, CF::NW>(asrc, 0, lds);
+  if constexpr (B_NK)
+    dma_issue<CF::B_ISSUE, CF::NW>(bsrc, 0, lds + CF::BM * BKF);
+  else
+    bt_load<CF>(B, ldb, N, n0, 0, breg);
+  for (int kt = 0; kt < KT; ++kt) {
+    uint16_t* cur = lds + (kt & 1) * CF::STAGE;
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this thread's copies of tile kt landed
+    if constexpr (!B_NK) bt_store<CF>(cur + CF::BM * BKF, breg);
+    __syncthreads();  // tile kt visible to all; everyone is done with tile kt-1's stage
+    if (kt + 1 < KT) {
+      uint16_t* nxt = lds + ((kt + 1) & 1) * CF::STAGE;
+      dma_issue<CF::A_ISSUE, CF::NW>(asrc, (kt + 1) * BKF, nxt);
+      if constexpr (B_NK)
+        dma_issue<CF::B_ISSUE, CF::NW>(bsrc, (kt + 1) * BKF, nxt + CF::BM * BKF);
+      else
+        bt_load<CF>(B, ldb, N, n0, (kt + 1) * BKF, breg);
+    }
+    compute_stage<CF>(cur, cur + CF::BM * BKF, acc);
+  }
+  __syncthreads();  // operand stages are free for the epilogue
+}
+
+// ---- [K][N] operand through LDS as stored, read with the gfx950 transpose load
+// The tile holds BKF rows (k) of BN columns (n), N-contiguous, in 32-byte
+// chunks; chunk c of row k sits at position c ^ tswz(k), so the 4 rows x 32 B
+// one 16-lane group reads, and the groups serviced together, hit distinct banks.
+__device__ __forceinline__ int tswz(int k) { return (k & 3) ^ ((k >> 1) & 4); }
+
+template <int BN>
+__device__ __forceinline__ int nofs(int k, int n) {  // element offset of (k, n) in the tile
+  return k * BN + ((((n >> 4) ^ tswz(k)) & (BN / 16 - 1)) << 4) + (n & 15);
+}
+
+// DMA sources: instruction i of wave w fills 1 KB = 1024 / (2 BN) rows.
+template <int BN, int ISSUE, int NW>
+__device__ __forceinline__ void dma_sources_kn(const uint16_t* __restrict__ base, int64_t ld, int N,
+                                               int n0, const uint16_t* (&src)[ISSUE]) {
+  constexpr int ROWS_PER_KB = 512 / BN;  // rows of BN bf16 in 1 KB
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < ISSUE; ++i) {
+    const int blk = wave + NW * i;
+    const int lane_bytes = lane * 16;
+    const int k = blk * ROWS_PER_KB + lane_bytes / (BN * 2);
+    const int pos = (lane_bytes % (BN * 2)) / 32;  // 32-byte chunk position in the row
+    const int half = (lane_bytes / 16) & 1;
+    const int c = (pos ^ tswz(k)) & (BN / 16 - 1);
+    const int gn = min(n0 + c * 16 + half * 8, N - 8);
+    src[i] = base + static_cast<int64_t>(k) * ld + gn;
+  }
+}
+
+template <int ISSUE, int NW>
+__device__ __forceinline__ void dma_issue_kn(const uint16_t* const* src, int64_t k0_times_ld,
+                                             uint16_t* tile) {
+  const int wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int i = 0; i < ISSUE; ++i)
+    __builtin_amdgcn_global_load_lds(src[i] + k0_times_ld, tile + (wave + NW * i) * 512, 16, 0, 0);
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+
+// B fragment (16 columns starting at nb, k = kb .. kb+7 per lane group) by two
+// transpose loads: lane L of a 16-lane group points at row kb + L/4, columns
+// nb + 4 (L%4); the load returns rows kb..kb+3 of column nb + L.
+template <int BN>
+__device__ __forceinline__ bf16x8_t tr_fragment(const uint16_t* tile, int kb, int nb) {
+  const int L = lane_id() & 15;
+  typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
+  const uint16_t* p0 = tile + nofs<BN>(kb + L / 4, nb + 4 * (L & 3));
+  const uint16_t* p1 = tile + nofs<BN>(kb + 4 + L / 4, nb + 4 * (L & 3));
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_v4*)((__attribute__((address_space(3))) uint16_t*)(p0)));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_v4*)((__attribute__((address_space(3))) uint16_t*)(p1)));
+  return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// C[BM x BN] = A[m0.., :] * B[:, n0..] with A [M][K] K-major and B [K][N]
+// N-major, both copied by DMA.  K % 64 == 0.
+template <class CF>
+__device__ __forceinline__ void mainloop_kn(const uint16_t* __restrict__ A, int64_t lda, int M,
+                                            int m0, const uint16_t* __restrict__ B, int64_t ldb,
+                                            int N, int n0, int K, uint16_t* lds,
+                                            f32x4_t (&acc)[CF::FM][CF::FN]) {
+  constexpr int B_ISSUE = CF::BN * BKF / 512 / CF::NW;  // 1 KB DMA blocks per thread
+  static_assert(B_ISSUE * 512 * CF::NW == CF::BN * BKF, "B tile splits into whole 1 KB blocks");
+#pragma unroll
+  for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* asrc[CF::A_ISSUE];
+  const uint16_t* bsrc[B_ISSUE];
+  dma_sources<CF::A_ISSUE, CF::NW>(A, lda, M, m0, asrc);
+  dma_sources_kn<CF::BN, B_ISSUE, CF::NW>(B, ldb, N, n0, bsrc);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  const int KT = K / BKF;
+  dma_issue<CF::A_ISSUE, CF::NW>(asrc, 0, lds);
+  dma_issue_kn<B_ISSUE, CF::NW>(bsrc, 0, lds + CF::BM * BKF);
+  for (int kt = 0; kt < KT; ++kt) {
+    uint16_t* cur = lds + (kt & 1) * CF::STAGE;
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+    __syncthreads();
+    if (kt + 1 < KT) {
+      uint16_t* nxt = lds + ((kt + 1) & 1) * CF::STAGE;
+      dma_issue<CF::A_ISSUE, CF::NW>(asrc, (kt + 1) * BKF, nxt);
+      dma_issue_kn<B_ISSUE, CF::NW>(bsrc, static_cast<int64_t>(kt + 1) * BKF * ldb,
+                                    nxt + CF::BM * BKF);
+    }
+    const uint16_t* sA = cur;
+    const uint16_t* sB = cur + CF::BM * BKF;
+#pragma unroll
+    for (int ks = 0; ks < BKF / 32; ++ks) {
+      const int kc = ks * 4 + (lane >> 4);
+      bf16x8_t a[CF::FM], b[CF::FN];
+#pragma unroll
+      for (int i = 0; i < CF::FM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(sA + tofs(wm * CF::WTM + i * 16 + (lane & 15), kc));
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j)
+        b[j] = tr_fragment<CF::BN>(sB, ks * 32 + (lane >> 4) * 8, wn * CF::WTN + j * 16);
+#pragma unroll
+      for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < CF::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  __syncthreads();
+}
+
+// Block index -> (m0, n0): blocks are dealt round-robin to the 8 XCDs, so the
+// grid is renumbered to give each XCD a contiguous run of tiles, walked in
+// groups of GROUP_M row blocks so concurrently running tiles share operands
+// in that XCD's L2.
+template <int GROUP_M>
+__device__ __forceinline__ void tile_coords(int m_blocks, int n_blocks, int BM, int BN, int& m0,
+                                            int& n0) {
+  const int G = m_blocks * n_blocks;
+  const int b = blockIdx.x;
+  int L = b;
+  if (G % 8 == 0) L = (b % 8) * (G / 8) + b / 8;
+  const int per_group = GROUP_M * n_blocks;
+  const int g = L / per_group;
+  const int first_m = g * GROUP_M;
+  const int gm = min(GROUP_M, m_blocks - first_m);
+  const int in = L - g * per_group;
+  m0 = (first_m + in % gm) * BM;
+  n0 = (in / gm) * BN;
+}
+
+}  // namespace fast
+
 // ---------------------------------------------------------------- G1 kernel
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(kThreads) void up_pack_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_up_t,
-    const float* __restrict__ bias, int M, int N, int K, int T, int C, int nt,
-    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
-    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
-  typedef Tile<BM, BN, WAVES_M, WAVES_N> TL;
-  constexpr int LDS_ST = BN + 8;  // staging pitch (elements)
-  static_assert(TL::WTM * LDS_ST <= TL::LDS_ELEMS, "staging fits in the operand buffers");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[TL::LDS_ELEMS];
-
-  const int n_blocks = (N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / n_blocks) * BM;
-  const int n0 = (blockIdx.x % n_blocks) * BN;
-
-  f32x4_t acc[TL::FM][TL::FN];
-  mfma_mainloop<BM, BN, WAVES_M, WAVES_N, true>(x, K, M, m0, w_up_t, K, N, n0, K, lds,
-                                                lds + BM * LDK, acc);
-
+// Epilogue of G1: h = ReLU(acc + b) rounded to bf16 is staged through LDS in
+// `passes` rounds of BM/passes rows (all rows at once when the staging area
+// holds the whole block, so no accumulator stays live while packing), then
+// every (row, tile) of the staged rows is packed by one wave.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int WTM, int WTN, int FM, int FN, int NT,
+          int PASSES>
+__device__ __forceinline__ void up_pack_epilogue(
+    const f32x4_t (&acc)[FM][FN], uint16_t* __restrict__ stage, const float* __restrict__ bias,
+    int m0, int n0, int M, int N, int T, int C, int nt, uint16_t* __restrict__ vals,
+    uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt, uint8_t* __restrict__ flags,
+    uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
+  static_assert(WAVES_M % PASSES == 0, "whole wave rows per pass");
+  constexpr int LDS_ST = BN + 8;                   // staging pitch (elements)
+  constexpr int ROWS = BM / PASSES;                // rows staged per pass
+  constexpr int WM_PER_PASS = WAVES_M / PASSES;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  float bj[TL::FN];
-#pragma unroll
-  for (int j = 0; j < TL::FN; ++j) {
-    const int col = n0 + wn * TL::WTN + j * 16 + (lane & 15);
-    bj[j] = col < N ? bias[col] : 0.f;
-  }
   const int tiles_per_block = BN / T;
-  uint16_t* stage = lds;
-
-  for (int p = 0; p < WAVES_M; ++p) {
+#pragma unroll 1
+  for (int p = 0; p < PASSES; ++p) {
     __syncthreads();
-    if (wm == p) {
+    if (wm / WM_PER_PASS == p) {
+      const int rofs = (wm % WM_PER_PASS) * WTM;
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * WTN + j * 16 + (lane & 15);
+        const float bj = n0 + col < N ? bias[n0 + col] : 0.f;
 #pragma unroll
-        for (int j = 0; j < TL::FN; ++j)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int row = i * 16 + (lane >> 4) * 4 + r;
-            const int col = wn * TL::WTN + j * 16 + (lane & 15);
-            const float z = acc[i][j][r] + bj[j];
+            const int row = rofs + i * 16 + (lane >> 4) * 4 + r;
+            const float z = acc[i][j][r] + bj;
             const float h = z > 0.f ? z : 0.f;  // ReLU; inactive units are +0.0
             stage[row * LDS_ST + col] = ElemTraits<uint16_t>::from_f32(h);
           }
+      }
     }
     __syncthreads();
-    const int rbase = m0 + p * TL::WTM;
-    for (int q = wave; q < TL::WTM * tiles_per_block; q += kThreads / kWave) {
+    const int rbase = m0 + p * ROWS;
+    for (int q = wave; q < ROWS * tiles_per_block; q += NT / kWave) {
       const int row = q / tiles_per_block;
       const int tt = q % tiles_per_block;
       const int n = rbase + row;
@@ -264,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void up_pack_bf16_kernel(
                                spill ? spill + static_cast<int64_t>(n) * N + col0 : nullptr);
     }
     if (hdebug != nullptr) {
-      for (int v = threadIdx.x; v < TL::WTM * (BN / 8); v += kThreads) {
+      for (int v = threadIdx.x; v < ROWS * (BN / 8); v += NT) {
         const int row = v / (BN / 8);
         const int cv = v % (BN / 8);
         const int n = rbase + row;
@@ -275,6 +557,46 @@ __global__ __launch_bounds__(kThreads) void up_pack_bf16_kernel(
       }
     }
   }
+}
+
+// Generic G1 (any K % 8 == 0): register-staged operands.
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(kThreads) void up_pack_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_up_t,
+    const float* __restrict__ bias, int M, int N, int K, int T, int C, int nt,
+    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
+  typedef Tile<BM, BN, WAVES_M, WAVES_N> TL;
+  static_assert(TL::WTM * (BN + 8) <= TL::LDS_ELEMS, "staging fits in the operand buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[TL::LDS_ELEMS];
+  const int n_blocks = (N + BN - 1) / BN;
+  const int m0 = (blockIdx.x / n_blocks) * BM;
+  const int n0 = (blockIdx.x % n_blocks) * BN;
+  f32x4_t acc[TL::FM][TL::FN];
+  mfma_mainloop<BM, BN, WAVES_M, WAVES_N, true>(x, K, M, m0, w_up_t, K, N, n0, K, lds,
+                                                lds + BM * LDK, acc);
+  up_pack_epilogue<BM, BN, WAVES_M, WAVES_N, TL::WTM, TL::WTN, TL::FM, TL::FN, kThreads, WAVES_M>(
+      acc, lds, bias, m0, n0, M, N, T, C, nt, vals, idx, cnt, flags, spill, hdebug);
+}
+
+// Fast G1 (K % 64 == 0).
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void up_pack_bf16_fast(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_up_t,
+    const float* __restrict__ bias, int M, int N, int K, int T, int C, int nt,
+    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
+  constexpr int STAGE_ELEMS = CF::BM * (CF::BN + 8);  // the whole block staged at once
+  constexpr int LDS_ELEMS = STAGE_ELEMS > 2 * CF::STAGE ? STAGE_ELEMS : 2 * CF::STAGE;
+  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "fits the 160 KB LDS of a CU");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  int m0, n0;
+  fast::tile_coords<4>((M + CF::BM - 1) / CF::BM, (N + CF::BN - 1) / CF::BN, CF::BM, CF::BN, m0, n0);
+  f32x4_t acc[CF::FM][CF::FN];
+  fast::mainloop<CF, true>(x, K, M, m0, w_up_t, K, N, n0, K, lds, acc);
+  up_pack_epilogue<CF::BM, CF::BN, CF::WAVES_M, CF::WAVES_N, CF::WTM, CF::WTN, CF::FM, CF::FN,
+                   CF::NT, 1>(acc, lds, bias, m0, n0, M, N, T, C, nt, vals, idx, cnt, flags, spill,
+                              hdebug);
 }
 
 // ---------------------------------------------------------------- G4 kernel
@@ -314,6 +636,44 @@ __global__ __launch_bounds__(kThreads) void fallback_bf16_kernel(
     }
 }
 
+// Fast G4 (K = d_ff, a multiple of 64): w_down tiles go to LDS as stored and
+// are read with the transpose load.  Tiles are numbered row-block-major over
+// the worst-case row count, so the live ones (a prefix) spread over all XCDs.
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void fallback_bf16_fast(
+    const uint16_t* __restrict__ dense_values, const int32_t* __restrict__ dense_rows,
+    const int32_t* __restrict__ n_dense, int64_t dense_cap, const uint16_t* __restrict__ w_down,
+    uint16_t* __restrict__ y, int64_t y_rows, int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+  const int M = static_cast<int>(min(static_cast<int64_t>(*n_dense), dense_cap));
+  const int n_blocks = (N + CF::BN - 1) / CF::BN;
+  const int m0 = (blockIdx.x / n_blocks) * CF::BM;
+  const int n0 = (blockIdx.x % n_blocks) * CF::BN;
+  if (m0 >= M) return;
+  f32x4_t acc[CF::FM][CF::FN];
+  fast::mainloop_kn<CF>(dense_values, K, M, m0, w_down, N, N, n0, K, lds, acc);
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+#pragma unroll
+  for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + wm * CF::WTM + i * 16 + (lane >> 4) * 4 + r;
+      if (m >= M) continue;
+      const int64_t yrow = dense_rows[m];
+      if (yrow < 0 || yrow >= y_rows) continue;  // never write outside y
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j) {
+        const int col = n0 + wn * CF::WTN + j * 16 + (lane & 15);
+        if (col < N) y[yrow * N + col] = ElemTraits<uint16_t>::from_f32(acc[i][j][r]);
+      }
+    }
+}
+
+typedef fast::Cfg<256, 256, 2, 4> BigCfg;
+typedef fast::Cfg<128, 128, 2, 4> MidCfg;
+
 }  // namespace
 
 hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint16_t* w_up_t,
@@ -323,7 +683,12 @@ hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint1
   auto* vals = static_cast<uint16_t*>(out.vals);
   auto* spill = static_cast<uint16_t*>(out.spill);
   auto* hdbg = static_cast<uint16_t*>(out.h_debug);
-  if (M >= 128) {
+  if (M >= 128 && K % 64 == 0) {
+    const int blocks = ((M + BigCfg::BM - 1) / BigCfg::BM) * ((N + BigCfg::BN - 1) / BigCfg::BN);
+    up_pack_bf16_fast<BigCfg><<<blocks, BigCfg::NT, 0, s>>>(
+        x, w_up_t, b_up, M, N, K, g.tile, g.capacity, g.n_tiles, vals, out.idx, out.cnt, out.flags,
+        spill, hdbg);
+  } else if (M >= 128) {
     constexpr int BM = 256, BN = 256;
     const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     up_pack_bf16_kernel<BM, BN, 2, 2><<<blocks, kThreads, 0, s>>>(
@@ -346,7 +711,12 @@ hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
   const int64_t worst = dense_cap < g.n_rows ? dense_cap : g.n_rows;
   if (worst <= 0) return hipSuccess;
   const int N = g.d_model, K = g.d_ff;
-  if (worst >= 128) {
+  if (worst >= 128 && K % 64 == 0 && N >= 128) {
+    const int64_t blocks =
+        ((worst + MidCfg::BM - 1) / MidCfg::BM) * ((N + MidCfg::BN - 1) / MidCfg::BN);
+    fallback_bf16_fast<MidCfg><<<static_cast<int>(blocks), MidCfg::NT, 0, s>>>(
+        dense_values, dense_rows, n_dense, dense_cap, w_down, y, g.n_rows, N, K);
+  } else if (worst >= 128) {
     constexpr int BM = 256, BN = 256;
     const int64_t blocks = ((worst + BM - 1) / BM) * ((N + BN - 1) / BN);
     fallback_bf16_kernel<BM, BN, 2, 2><<<static_cast<int>(blocks), kThreads, 0, s>>>(

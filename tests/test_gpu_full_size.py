@@ -1,0 +1,79 @@
+"""Parity at the benchmark workloads' full sizes, through the same entry
+point and launch configuration bench.py times.
+
+The oracle cannot redo every row of the larger layers in seconds, so these
+tests check (a) the packing bit-exactly on every row where that is cheap
+(tile counts, the dense-row list) and on sampled rows for the slots and dense
+rows, against the oracle's packer applied to the GPU's own h, (b) h and y of
+sampled rows against the oracle's float64 FFN, within the stated tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from activation_sparse_transformer_amd import twell
+from activation_sparse_transformer_amd.synth import CONFIGS, make_inputs
+from gpu_helpers import TOL, as_f32, as_f64, assert_close_rel, oracle_inputs, say, u32
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {"tiny_fp32": 64, "ffn_1b_bf16": 96, "hybrid_stress_bf16": 48, "decode_bf16": 16,
+           "large_bf16": 24}
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_full_size_forward(name):
+    cfg = CONFIGS[name]
+    say(f"full-size {name}: generating inputs")
+    t = make_inputs(cfg)
+    d = {k: v.cuda() for k, v in t.items()}
+    say(f"full-size {name}: forward")
+    out = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
+                                   cfg.capacity, debug_h=True)
+    torch.cuda.synchronize()
+    assert int(out.status.item()) == twell.TWELL_OK
+    N, T, C = cfg.n_rows, cfg.tile, cfg.capacity
+    hy = out.hybrid
+
+    # every row: tile counts and the dense-row list, from the GPU's own h
+    say(f"full-size {name}: routing of every row")
+    dense = np.zeros(N, dtype=bool)
+    for r0 in range(0, N, 1024):
+        hc = as_f32(out.h_debug[r0:r0 + 1024])
+        cnt = oracle.tile_counts(hc, T)
+        dense[r0:r0 + 1024] = (cnt > C).any(axis=1)
+        gpu_cnt = hy.counts[r0:r0 + 1024].cpu().numpy()
+        expect = np.where((cnt > C).any(axis=1)[:, None], 0, cnt)
+        np.testing.assert_array_equal(gpu_cnt, expect)
+    dense_rows = np.nonzero(dense)[0]
+    n_dense = hy.n_dense_host()
+    assert n_dense == len(dense_rows)
+    np.testing.assert_array_equal(hy.dense_rows[:n_dense].cpu().numpy(), dense_rows)
+    say(f"  n_dense = {n_dense} of {N}")
+
+    # sampled rows: slots, dense rows, h and y
+    rng = np.random.default_rng(1234)
+    k = min(SAMPLES[name], N)
+    rows = np.sort(rng.choice(N, size=k, replace=False))
+    if n_dense:  # make sure dense rows are among the samples
+        rows = np.unique(np.concatenate([rows, dense_rows[:: max(1, n_dense // 8)][:8]]))
+    say(f"full-size {name}: {len(rows)} sampled rows")
+    h_rows = as_f32(out.h_debug[torch.as_tensor(rows, device="cuda")])
+    ref = oracle.pack(h_rows, T, C)
+    sel = torch.as_tensor(rows, device="cuda")
+    np.testing.assert_array_equal(hy.counts[sel].cpu().numpy(), ref.counts)
+    np.testing.assert_array_equal(hy.indices[sel].cpu().numpy(), ref.indices)
+    np.testing.assert_array_equal(u32(as_f32(hy.values[sel])), u32(ref.values))
+    pos = {int(r): m for m, r in enumerate(dense_rows)}
+    for i, r in enumerate(rows):
+        if int(r) in pos:
+            m = pos[int(r)]
+            np.testing.assert_array_equal(u32(as_f32(hy.dense_values[m])), u32(h_rows[i]))
+
+    x, w_up_t, b, w_down = oracle_inputs(t)
+    h_ref, y_ref = oracle.ffn_forward_rows(x, w_up_t, b, w_down, rows)
+    tol = TOL[cfg.torch_dtype]
+    assert_close_rel(h_rows.astype(np.float64), h_ref, tol, "h")
+    err, scale = assert_close_rel(as_f64(out.y[sel]), y_ref, tol, "y")
+    say(f"  y max|err| {err:.3e} vs tol*max|y| {tol * scale:.3e}")

@@ -138,6 +138,12 @@ SMALL = [
     ("hybrid_stress_bf16", 260, 264, 1152),
     ("decode_bf16", 16, 512, 1024),
     ("large_bf16", 129, 136, 768),
+    # K a multiple of 64 and >= 128 rows: the direct-to-LDS MFMA kernels,
+    # with ragged row counts and partial column blocks
+    ("ffn_1b_bf16", 300, 256, 640),
+    ("hybrid_stress_bf16", 520, 512, 1536),
+    ("large_bf16", 257, 192, 1280),
+    ("decode_bf16", 16, 256, 512),
 ]
 
 
