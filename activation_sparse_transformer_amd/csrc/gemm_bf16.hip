@@ -229,7 +229,6 @@ struct Cfg {
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static constexpr int A_ISSUE = BM / (8 * NW);  // DMA instructions per thread per stage
   static constexpr int B_ISSUE = BN / (8 * NW);
-  static constexpr int BT_ITEMS = ((BN / 8) * (BKF / 4) + NT - 1) / NT;  // 4x8 blocks per thread
   static constexpr int STAGE = (BM + BN) * BKF;                // elements per LDS stage
   static_assert(A_ISSUE * 8 * NW == BM && B_ISSUE * 8 * NW == BN, "whole 1 KB blocks per wave");
   static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "16x16 blocks");
@@ -260,101 +259,65 @@ __device__ __forceinline__ void dma_issue(const uint16_t* const* src, int k0, ui
     __builtin_amdgcn_global_load_lds(src[i] + k0, tile + (wave + NW * i) * 512, 16, 0, 0);
 }
 
-// [K][N] operand: item (nv, kq) = rows k0+4kq..+3, columns n0+8nv..+7.
-template <class CF>
-__device__ __forceinline__ void bt_load(const uint16_t* __restrict__ B, int64_t ldb, int N, int n0,
-                                        int k0, uint4 (&reg)[CF::BT_ITEMS][4]) {
-  static_assert(CF::BT_ITEMS * CF::NT == (CF::BN / 8) * (BKF / 4), "transposed B splits evenly");
-#pragma unroll
-  for (int it = 0; it < CF::BT_ITEMS; ++it) {
-    const int item = threadIdx.x + it * CF::NT;
-    const int nv = item % (CF::BN / 8), kq = item / (CF::BN / 8);
-    const int gn = min(n0 + nv * 8, N - 8);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      reg[it][r] = *reinterpret_cast<const uint4*>(B + static_cast<int64_t>(k0 + kq * 4 + r) * ldb + gn);
-  }
-}
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
+// One LDS stage of C += A B^T on v_mfma_f32_32x32x16_bf16: lane l of a
+// fragment holds row (l & 31) and the 8 k's of 16-byte chunk kc = 2 ks + l/32.
 template <class CF>
-__device__ __forceinline__ void bt_store(uint16_t* __restrict__ tile, const uint4 (&reg)[CF::BT_ITEMS][4]) {
-#pragma unroll
-  for (int it = 0; it < CF::BT_ITEMS; ++it) {
-    const int item = threadIdx.x + it * CF::NT;
-    const int nv = item % (CF::BN / 8), kq = item / (CF::BN / 8);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      uint32_t d[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) d[r] = pick(reg[it][r], n / 2);
-      const uint32_t lo = (n & 1) ? ((d[0] >> 16) | (d[1] & 0xffff0000u)) : ((d[0] & 0xffffu) | (d[1] << 16));
-      const uint32_t hi = (n & 1) ? ((d[2] >> 16) | (d[3] & 0xffff0000u)) : ((d[2] & 0xffffu) | (d[3] << 16));
-      const int row = nv * 8 + n;
-      *reinterpret_cast<uint2*>(tile + tofs(row, kq >> 1) + (kq & 1) * 4) = make_uint2(lo, hi);
-    }
-  }
-}
-
-template <class CF>
-__device__ __forceinline__ void compute_stage(const uint16_t* __restrict__ sA,
-                                              const uint16_t* __restrict__ sB,
-                                              f32x4_t (&acc)[CF::FM][CF::FN]) {
+__device__ __forceinline__ void compute_stage32(const uint16_t* __restrict__ sA,
+                                                const uint16_t* __restrict__ sB,
+                                                f32x16_t (&acc)[CF::WTM / 32][CF::WTN / 32]) {
+  constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
 #pragma unroll
-  for (int ks = 0; ks < BKF / 32; ++ks) {
-    const int kc = ks * 4 + (lane >> 4);
-    bf16x8_t a[CF::FM], b[CF::FN];
+  for (int ks = 0; ks < BKF / 16; ++ks) {
+    const int kc = ks * 2 + (lane >> 5);
+    bf16x8_t a[FM], b[FN];
 #pragma unroll
-    for (int i = 0; i < CF::FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(sA + tofs(wm * CF::WTM + i * 16 + (lane & 15), kc));
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t*>(sA + tofs(wm * CF::WTM + i * 32 + (lane & 31), kc));
 #pragma unroll
-    for (int j = 0; j < CF::FN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t*>(sB + tofs(wn * CF::WTN + j * 16 + (lane & 15), kc));
+    for (int j = 0; j < FN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8_t*>(sB + tofs(wn * CF::WTN + j * 32 + (lane & 31), kc));
 #pragma unroll
-    for (int i = 0; i < CF::FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < CF::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
 }
 
-// C[BM x BN] = A[m0.., :] B^T with A [M][K] K-major and B either [N][K]
-// (B_NK) or [K][N].  K % 64 == 0.  `lds` holds two stages.
-template <class CF, bool B_NK>
-__device__ __forceinline__ void mainloop(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
-                                         const uint16_t* __restrict__ B, int64_t ldb, int N, int n0,
-                                         int K, uint16_t* lds, f32x4_t (&acc)[CF::FM][CF::FN]) {
+// C[BM x BN] = A[m0.., :] B[n0.., :]^T, A [M][K] and B [N][K] both K-major,
+// K % 64 == 0, both operands copied by DMA.  `lds` holds two stages.
+template <class CF>
+__device__ __forceinline__ void mainloop32(const uint16_t* __restrict__ A, int64_t lda, int M,
+                                           int m0, const uint16_t* __restrict__ B, int64_t ldb,
+                                           int N, int n0, int K, uint16_t* lds,
+                                           f32x16_t (&acc)[CF::WTM / 32][CF::WTN / 32]) {
 #pragma unroll
-  for (int i = 0; i < CF::FM; ++i)
+  for (int i = 0; i < CF::WTM / 32; ++i)
 #pragma unroll
-    for (int j = 0; j < CF::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < CF::WTN / 32; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const uint16_t* asrc[CF::A_ISSUE];
+  const uint16_t* bsrc[CF::B_ISSUE];
   dma_sources<CF::A_ISSUE, CF::NW>(A, lda, M, m0, asrc);
-  const uint16_t* bsrc[B_NK ? CF::B_ISSUE : 1];
-  uint4 breg[B_NK ? 1 : CF::BT_ITEMS][4];
-  if constexpr (B_NK) dma_sources<CF::B_ISSUE, CF::NW>(B, ldb, N, n0, bsrc);
-
+  dma_sources<CF::B_ISSUE, CF::NW>(B, ldb, N, n0, bsrc);
   const int KT = K / BKF;
   dma_issue<CF::A_ISSUE, CF::NW>(asrc, 0, lds);
-  if constexpr (B_NK)
-    dma_issue<CF::B_ISSUE, CF::NW>(bsrc, 0, lds + CF::BM * BKF);
-  else
-    bt_load<CF>(B, ldb, N, n0, 0, breg);
+  dma_issue<CF::B_ISSUE, CF::NW>(bsrc, 0, lds + CF::BM * BKF);
   for (int kt = 0; kt < KT; ++kt) {
     uint16_t* cur = lds + (kt & 1) * CF::STAGE;
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this thread's copies of tile kt landed
-    if constexpr (!B_NK) bt_store<CF>(cur + CF::BM * BKF, breg);
     __syncthreads();  // tile kt visible to all; everyone is done with tile kt-1's stage
     if (kt + 1 < KT) {
       uint16_t* nxt = lds + ((kt + 1) & 1) * CF::STAGE;
       dma_issue<CF::A_ISSUE, CF::NW>(asrc, (kt + 1) * BKF, nxt);
-      if constexpr (B_NK)
-        dma_issue<CF::B_ISSUE, CF::NW>(bsrc, (kt + 1) * BKF, nxt + CF::BM * BKF);
-      else
-        bt_load<CF>(B, ldb, N, n0, (kt + 1) * BKF, breg);
+      dma_issue<CF::B_ISSUE, CF::NW>(bsrc, (kt + 1) * BKF, nxt + CF::BM * BKF);
     }
-    compute_stage<CF>(cur, cur + CF::BM * BKF, acc);
+    compute_stage32<CF>(cur, cur + CF::BM * BKF, acc);
   }
   __syncthreads();  // operand stages are free for the epilogue
 }
@@ -579,24 +542,197 @@ __global__ __launch_bounds__(kThreads) void up_pack_bf16_kernel(
       acc, lds, bias, m0, n0, M, N, T, C, nt, vals, idx, cnt, flags, spill, hdebug);
 }
 
-// Fast G1 (K % 64 == 0).
+// Epilogue of the fast G1, straight from the 32x32 MFMA accumulators (no
+// staging of h).  In that layout register r of lane l holds row
+// (r/4)*8 + (l/32)*4 + r%4 and column l%32 of a 32x32 block, so one ballot per
+// (block, register) yields, in each 32-bit half, the non-zero pattern of 32
+// consecutive columns of one row.  A wave owns 64 columns (a "segment") of
+// 128 rows; a tile of width T spans T/64 segments of adjacent waves:
+//   1. h = ReLU(acc + b) rounded to bf16, in place;
+//   2. each wave counts the non-zeros of each of its row segments and posts
+//      the counts to LDS (one byte per (row, segment));
+//   3. after a barrier every lane knows, for its row, the tile's total and the
+//      non-zeros in the segments to its left, so each non-zero element knows
+//      its slot (column order) and is stored there directly; the tile's first
+//      wave writes the count, the overflow flag and the padding slots; a tile
+//      over capacity spills its raw h instead.
+// When a block's slots of one row fit in 64 (tiles per block x C <= 64), the
+// slots, counts and flags are assembled in LDS (zero-filled, so padding needs
+// no stores) and copied out with coalesced stores; otherwise each slot is
+// stored to global memory where it is found.
+constexpr int kStagedSlots = 64;
+
+template <class CF, bool STAGED>
+__device__ __forceinline__ void up_pack_epilogue32(
+    const fast::f32x16_t (&acc)[CF::WTM / 32][CF::WTN / 32], uint8_t* __restrict__ lds,
+    const float* __restrict__ bias, int m0, int n0, int M, int N, int T, int C, int nt,
+    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
+  constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32, BM = CF::BM;
+  static_assert(CF::WTN == 64 && FN == 2 && CF::WAVES_N == 4, "64-column segments, 4 per row");
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  // LDS: per-(row, segment) counts, then (staged) slot values, indices, counts, flags
+  uint8_t* seg = lds;                                            // [BM][4]
+  uint16_t* sv = reinterpret_cast<uint16_t*>(lds + BM * 4);      // [BM][kStagedSlots]
+  uint8_t* si = lds + BM * 4 + BM * kStagedSlots * 2;            // [BM][kStagedSlots]
+  uint8_t* sc = si + BM * kStagedSlots;                          // [BM][4]
+  uint8_t* sf = sc + BM * 4;                                     // [BM][4]
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  const int hh = lane >> 5, c = lane & 31;
+  const int seg_col = n0 + wn * 64;   // first column of this wave's segment
+  const bool seg_ok = seg_col < N;    // segments (and tiles) are all-in or all-out
+  const int spt = T / 64;             // segments per tile
+  const int first = wn & ~(spt - 1);  // first segment of this wave's tile
+  const int t = seg_col / T;          // global tile index
+  const int tb = (wn * 64) / T;       // tile index inside the block
+  const int tpb = CF::BN / T;         // tiles per block
+  const uint32_t below = (1u << c) - 1u;
+  // byte masks selecting the tile's segments, and those left of this wave
+  const uint32_t tile_mask = (spt == 4 ? 0x01010101u : spt == 2 ? 0x0101u : 0x01u) << (8 * first);
+  const int nleft = wn - first;        // segments of the tile left of this wave (0..3)
+  const uint32_t left_mask = nleft == 0 ? 0u : (0x01010101u >> (8 * (4 - nleft))) << (8 * first);
+  if constexpr (STAGED) {
+    for (int e = threadIdx.x; e < BM * kStagedSlots / 2; e += CF::NT) {
+      reinterpret_cast<uint32_t*>(sv)[e] = 0u;
+      if (e < BM * kStagedSlots / 4) reinterpret_cast<uint32_t*>(si)[e] = 0u;
+    }
+  }
+  float bj[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = seg_col + j * 32 + c;
+    bj[j] = col < N ? bias[col] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    // 1. h = ReLU(acc + b) as bf16 (+0.0 when off), two rows per register, RNE
+    uint32_t hp[FN][8];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float z0 = acc[i][j][r] + bj[j], z1 = acc[i][j][r + 1] + bj[j];
+        const f32x2_t z = {z0 > 0.f ? z0 : 0.f, z1 > 0.f ? z1 : 0.f};
+        hp[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2_t));
+      }
+    auto hv = [&](int j, int r) -> uint32_t {
+      return (r & 1) ? (hp[j][r / 2] >> 16) : (hp[j][r / 2] & 0xffffu);
+    };
+    auto half = [&](uint64_t m) -> uint32_t {
+      return hh ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
+    };
+    // 2. non-zero pattern per (row, segment); counts to LDS
+    uint32_t c0[16], c1[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      c0[r] = half(wave_ballot(hv(0, r) != 0u));
+      c1[r] = half(wave_ballot(hv(1, r) != 0u));
+    }
+    const int rl0 = wm * CF::WTM + i * 32 + hh * 4;  // row of register r = rl0 + (r/4)*8 + r%4
+    if (c == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        seg[(rl0 + (r >> 2) * 8 + (r & 3)) * 4 + wn] = static_cast<uint8_t>(__popc(c0[r]) + __popc(c1[r]));
+    }
+    __syncthreads();
+    // 3. slots, metadata, spill
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rl = rl0 + (r >> 2) * 8 + (r & 3);
+      const int n = m0 + rl;
+      const uint32_t counts = *reinterpret_cast<const uint32_t*>(seg + rl * 4);
+      const int total = static_cast<int>(__builtin_amdgcn_udot4(counts, tile_mask, 0u, false));
+      const int left = static_cast<int>(__builtin_amdgcn_udot4(counts, left_mask, 0u, false));
+      const bool fits = total <= C;
+      const bool row_ok = seg_ok && n < M;
+      const int pos0 = left;
+      const int pos1 = left + __popc(c0[r]);
+      const int64_t slot0 = (static_cast<int64_t>(n) * nt + t) * C;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const uint32_t v = hv(j, r);
+        const int col = seg_col + j * 32 + c;
+        if (row_ok && v != 0u && fits) {
+          const int pos = (j ? pos1 : pos0) + __popc((j ? c1[r] : c0[r]) & below);
+          if constexpr (STAGED) {
+            sv[rl * kStagedSlots + tb * C + pos] = static_cast<uint16_t>(v);
+            si[rl * kStagedSlots + tb * C + pos] = static_cast<uint8_t>(col - t * T);
+          } else {
+            vals[slot0 + pos] = static_cast<uint16_t>(v);
+            idx[slot0 + pos] = static_cast<uint8_t>(col - t * T);
+          }
+        }
+        if (row_ok && !fits && spill != nullptr)
+          spill[static_cast<int64_t>(n) * N + col] = static_cast<uint16_t>(v);
+        if (row_ok && hdebug != nullptr)
+          hdebug[static_cast<int64_t>(n) * N + col] = static_cast<uint16_t>(v);
+      }
+      if (row_ok && wn == first) {
+        if constexpr (STAGED) {
+          if (c == 0) {
+            sc[rl * 4 + tb] = static_cast<uint8_t>(fits ? total : 0);
+            sf[rl * 4 + tb] = static_cast<uint8_t>(fits ? 0 : 1);
+          }
+        } else {
+          if (c == 0) {
+            cnt[static_cast<int64_t>(n) * nt + t] = static_cast<uint8_t>(fits ? total : 0);
+            flags[static_cast<int64_t>(n) * nt + t] = static_cast<uint8_t>(fits ? 0 : 1);
+          }
+          if (fits)
+            for (int sl = total + c; sl < C; sl += 32) {
+              vals[slot0 + sl] = 0;
+              idx[slot0 + sl] = 0;
+            }
+        }
+      }
+    }
+  }
+  if constexpr (STAGED) {
+    __syncthreads();
+    // copy the block's slots out: each row owns one contiguous run per array
+    const int t0 = n0 / T;
+    const int tv = min(tpb, nt - t0);  // tiles of the block inside d_ff
+    const int run = tv * C;
+    for (int e = threadIdx.x; e < BM * run; e += CF::NT) {
+      const int rl = e / run, k = e - (e / run) * run;
+      const int n = m0 + rl;
+      if (n < M) {
+        const int64_t g = (static_cast<int64_t>(n) * nt + t0) * C + k;
+        vals[g] = sv[rl * kStagedSlots + k];
+        idx[g] = si[rl * kStagedSlots + k];
+      }
+    }
+    for (int e = threadIdx.x; e < BM * tv; e += CF::NT) {
+      const int rl = e / tv, k = e - (e / tv) * tv;
+      const int n = m0 + rl;
+      if (n < M) {
+        cnt[static_cast<int64_t>(n) * nt + t0 + k] = sc[rl * 4 + k];
+        flags[static_cast<int64_t>(n) * nt + t0 + k] = sf[rl * 4 + k];
+      }
+    }
+  }
+}
+
+// Fast G1 (K % 64 == 0): 32x32x16 MFMA mainloop, pack straight from registers.
 template <class CF>
 __global__ __launch_bounds__(CF::NT) void up_pack_bf16_fast(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_up_t,
     const float* __restrict__ bias, int M, int N, int K, int T, int C, int nt,
     uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
     uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
-  constexpr int STAGE_ELEMS = CF::BM * (CF::BN + 8);  // the whole block staged at once
-  constexpr int LDS_ELEMS = STAGE_ELEMS > 2 * CF::STAGE ? STAGE_ELEMS : 2 * CF::STAGE;
-  static_assert(LDS_ELEMS * 2 <= 160 * 1024, "fits the 160 KB LDS of a CU");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
   int m0, n0;
   fast::tile_coords<4>((M + CF::BM - 1) / CF::BM, (N + CF::BN - 1) / CF::BN, CF::BM, CF::BN, m0, n0);
-  f32x4_t acc[CF::FM][CF::FN];
-  fast::mainloop<CF, true>(x, K, M, m0, w_up_t, K, N, n0, K, lds, acc);
-  up_pack_epilogue<CF::BM, CF::BN, CF::WAVES_M, CF::WAVES_N, CF::WTM, CF::WTN, CF::FM, CF::FN,
-                   CF::NT, 1>(acc, lds, bias, m0, n0, M, N, T, C, nt, vals, idx, cnt, flags, spill,
-                              hdebug);
+  fast::f32x16_t acc[CF::WTM / 32][CF::WTN / 32];
+  fast::mainloop32<CF>(x, K, M, m0, w_up_t, K, N, n0, K, lds, acc);
+  if ((CF::BN / T) * C <= kStagedSlots)
+    up_pack_epilogue32<CF, true>(acc, reinterpret_cast<uint8_t*>(lds), bias, m0, n0, M, N, T, C,
+                                 nt, vals, idx, cnt, flags, spill, hdebug);
+  else
+    up_pack_epilogue32<CF, false>(acc, reinterpret_cast<uint8_t*>(lds), bias, m0, n0, M, N, T, C,
+                                  nt, vals, idx, cnt, flags, spill, hdebug);
 }
 
 // ---------------------------------------------------------------- G4 kernel
