@@ -142,6 +142,136 @@ __global__ __launch_bounds__(kThreads) void spmm_sparse_kernel(
   }
 }
 
+// ---------------------------------------------------------------- XCD-sliced
+// Workgroups are dealt round-robin to the 8 XCDs, and each XCD has its own
+// L2.  Here XCD x owns column slice (x mod n_slices) of w_down and y, so the
+// rows it gathers stay in its L2 (d_model/8 columns x d_ff rows).  Each wave
+// takes one row at a time over its slice: VEC consecutive columns per lane.
+// bf16 products use v_dot2_f32_bf16 with one half of the value operand zero:
+// y[c] += v*W[c] as a single exact-product, single-rounding step per element.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+template <int VEC>
+struct WVec;
+template <>
+struct WVec<4> {
+  uint32_t d[2];
+};
+template <>
+struct WVec<8> {
+  uint32_t d[4];
+};
+template <>
+struct WVec<16> {
+  uint32_t d[8];
+};
+
+template <int VEC>
+__device__ __forceinline__ void load_wvec(WVec<VEC>& o, const uint16_t* p) {
+  if constexpr (VEC == 4) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    o.d[0] = q.x, o.d[1] = q.y;
+  } else {
+#pragma unroll
+    for (int h = 0; h < VEC / 8; ++h) {
+      const uint4 q = *reinterpret_cast<const uint4*>(p + 8 * h);
+      o.d[4 * h] = q.x, o.d[4 * h + 1] = q.y, o.d[4 * h + 2] = q.z, o.d[4 * h + 3] = q.w;
+    }
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void dot2_row(float (&acc)[VEC], uint32_t vlo, uint32_t vhi,
+                                         const WVec<VEC>& w) {
+  const bf16x2_t a0 = __builtin_bit_cast(bf16x2_t, vlo);  // (v, 0)
+  const bf16x2_t a1 = __builtin_bit_cast(bf16x2_t, vhi);  // (0, v)
+#pragma unroll
+  for (int i = 0; i < VEC / 2; ++i) {
+    const bf16x2_t b = __builtin_bit_cast(bf16x2_t, w.d[i]);
+    acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(a0, b, acc[2 * i], false);
+    acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(a1, b, acc[2 * i + 1], false);
+  }
+}
+
+// Each wave takes one row of its XCD's column slice at a time: it first
+// compacts the row's live slots into a per-wave LDS list (byte offset of the
+// w_down row, value) with a ballot prefix, then walks the list 8 entries at a
+// time with broadcast LDS reads, keeping 8 row gathers in flight.
+constexpr int kListUnroll = 8;
+
+template <int VEC>
+__global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
+    const uint16_t* __restrict__ vals, const uint8_t* __restrict__ idx,
+    const uint8_t* __restrict__ cnt, const int32_t* __restrict__ row_map,
+    const uint16_t* __restrict__ w, uint16_t* __restrict__ y, int64_t N, int dm, int T, int C,
+    int nt, int n_slices) {
+  extern __shared__ uint2 spmm_lists[];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int nslots = nt * C;
+  uint2* list = spmm_lists + wave * nslots;
+  const int xcd = blockIdx.x % 8;
+  const int slice = xcd % n_slices;
+  const int parts = 8 / n_slices;  // XCDs sharing this slice split its rows
+  const int part = xcd / n_slices;
+  const int64_t per_xcd_waves = static_cast<int64_t>(gridDim.x / 8) * kWavesPerBlock;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x / 8) * kWavesPerBlock + wave;
+  const int col = slice * (kWave * VEC) + lane * VEC;
+  const char* wbase = reinterpret_cast<const char*>(w + col);
+  for (int64_t n = part + parts * wid; n < N; n += parts * per_xcd_waves) {
+    if (row_map != nullptr && row_map[n] >= 0) continue;  // dense row: the fallback GEMM writes it
+    const int64_t s0 = n * nslots;
+    int nnz = 0;
+    for (int g = 0; g < nslots; g += kWave) {
+      const int s = g + lane;
+      bool live = false;
+      uint32_t off = 0, v = 0;
+      if (s < nslots) {
+        const int t = s / C;
+        const int k = s - t * C;
+        if (k < static_cast<int>(cnt[n * nt + t])) {
+          const int local = static_cast<int>(idx[s0 + s]);
+          live = local < T;  // a malformed index is ignored rather than read out of bounds
+          off = static_cast<uint32_t>(t * T + local) * static_cast<uint32_t>(dm) * 2u;
+          v = vals[s0 + s];
+        }
+      }
+      const uint64_t m = wave_ballot(live);
+      if (live) list[nnz + popc_below(m)] = make_uint2(off, v);
+      nnz += popc64(m);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's list is in LDS
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int k = 0; k < nnz; k += kListUnroll) {
+      uint2 e[kListUnroll];
+      WVec<VEC> wv[kListUnroll];
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u) {
+        e[u] = list[min(k + u, nnz - 1)];  // past the end: reread the last entry, unused
+        load_wvec<VEC>(wv[u], reinterpret_cast<const uint16_t*>(wbase + e[u].x));
+      }
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u)
+        if (k + u < nnz) dot2_row<VEC>(acc, e[u].y, e[u].y << 16, wv[u]);
+    }
+    uint32_t out[VEC / 2];
+#pragma unroll
+    for (int i = 0; i < VEC / 2; ++i)
+      out[i] = static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * i])) |
+               (static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * i + 1])) << 16);
+    uint16_t* dst = y + n * dm + col;
+    if constexpr (VEC == 4) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(out[0], out[1]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < VEC / 8; ++h)
+        *reinterpret_cast<uint4*>(dst + 8 * h) =
+            make_uint4(out[4 * h], out[4 * h + 1], out[4 * h + 2], out[4 * h + 3]);
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
@@ -154,6 +284,33 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
   const int64_t want = (items + kWavesPerBlock - 1) / kWavesPerBlock;
   const unsigned blocks = static_cast<unsigned>(want < 16384 ? want : 16384);
   if (elem_bytes == 2) {
+    // Column slices of 64 lanes x 8 bf16 (x 16 when d_model/8 needs it), one
+    // per XCD or shared by 2, 4, 8 XCDs; slot lists must fit in LDS.
+    int n_slices = 0, vec = 0;
+    if (g.d_model % 512 == 0) {
+      const int ns = g.d_model / 512;
+      if (ns == 1 || ns == 2 || ns == 4 || ns == 8) n_slices = ns, vec = 8;
+      else if (ns == 16) n_slices = 8, vec = 16;
+    }
+    const size_t list_bytes = static_cast<size_t>(kWavesPerBlock) * g.n_tiles * g.capacity * 8;
+    const bool offsets_fit = static_cast<int64_t>(g.d_ff) * g.d_model * 2 < (int64_t{1} << 32);
+    if (n_slices > 0 && list_bytes <= 64 * 1024 && offsets_fit) {
+      const int64_t rows_per_xcd = (g.n_rows + (8 / n_slices) - 1) / (8 / n_slices);
+      const int64_t wg_per_xcd = (rows_per_xcd + kWavesPerBlock - 1) / kWavesPerBlock;
+      const unsigned xblocks = static_cast<unsigned>(8 * (wg_per_xcd < 512 ? wg_per_xcd : 512));
+      const uint16_t* v16 = static_cast<const uint16_t*>(vals);
+      const uint16_t* w16 = static_cast<const uint16_t*>(w_down);
+      uint16_t* y16 = static_cast<uint16_t*>(y);
+      if (vec == 8)
+        spmm_list_bf16_kernel<8><<<xblocks, kThreads, list_bytes, s>>>(
+            v16, idx, cnt, row_map, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
+            n_slices);
+      else
+        spmm_list_bf16_kernel<16><<<xblocks, kThreads, list_bytes, s>>>(
+            v16, idx, cnt, row_map, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
+            n_slices);
+      return hipGetLastError();
+    }
     spmm_sparse_kernel<uint16_t><<<blocks, kThreads, 0, s>>>(
         static_cast<const uint16_t*>(vals), idx, cnt, row_map, static_cast<const uint16_t*>(w_down),
         static_cast<uint16_t*>(y), g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles, n_chunks);

@@ -84,7 +84,8 @@ def test_pack_zero_rows():
 
 # ------------------------------------------------------------------------ spmm
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("n,dm,T,C", [(50, 136, 64, 4), (300, 520, 128, 4), (130, 64, 256, 8)])
+@pytest.mark.parametrize("n,dm,T,C", [(50, 136, 64, 4), (300, 520, 128, 4), (130, 64, 256, 8),
+                                      (70, 2048, 128, 4), (33, 4096, 64, 2), (20, 8192, 256, 8)])
 def test_spmm_integer_exact(dtype, n, dm, T, C):
     say(f"spmm integer {dtype} n={n} dm={dm} T={T}")
     rng = np.random.default_rng(n + dm)
@@ -144,6 +145,10 @@ SMALL = [
     ("hybrid_stress_bf16", 520, 512, 1536),
     ("large_bf16", 257, 192, 1280),
     ("decode_bf16", 16, 256, 512),
+    # d_model/8 a whole 4, 8 or 16 bf16 per lane: the XCD-sliced sparse product
+    ("ffn_1b_bf16", 150, 2048, 512),
+    ("hybrid_stress_bf16", 40, 4096, 384),
+    ("large_bf16", 24, 8192, 512),
 ]
 
 
