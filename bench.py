@@ -39,11 +39,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3
 STAGES = ("up_gemm_pack", "route", "spmm_sparse", "fallback_gemm")
+# kernels each stage launches for bf16 layers with d_model a multiple of 512
 STAGE_KERNELS = {
-    "up_gemm_pack": "up_pack_bf16_kernel",
+    "up_gemm_pack": "up_pack_bf16_fast",
     "route": "route_scan_kernel + materialize_kernel",
-    "spmm_sparse": "spmm_sparse_kernel",
-    "fallback_gemm": "fallback_bf16_kernel",
+    "spmm_sparse": "spmm_list_bf16_kernel",
+    "fallback_gemm": "fallback_bf16_fast",
 }
 
 
