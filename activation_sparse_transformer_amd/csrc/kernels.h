@@ -37,12 +37,21 @@ hipError_t launch_up_pack_f32(const Geometry& g, const float* x, const float* w_
 hipError_t launch_pack_tiles(const Geometry& g, const void* h, int elem_bytes, const PackOut& out,
                              hipStream_t s);
 
-// G2a: per-row OR of the tile flags, ascending numbering of dense rows.
-//   row_map[n] = dense index m, or -1 for a sparse row; dense_rows[m] = n for
-//   m < dense_cap; *n_dense = total; *status = OK / DENSE_CAPACITY.
-hipError_t launch_route_scan(const Geometry& g, const uint8_t* flags, int32_t* row_map,
-                             int32_t* dense_rows, int64_t dense_cap, int32_t* n_dense,
-                             int32_t* status, hipStream_t s);
+// Routing scratch (workspace).
+struct RouteBufs {
+  uint8_t* flags;        // [N][nt] 1 when the tile overflowed (written by the pack step)
+  uint8_t* row_dense;    // [N] 1 when any tile of the row overflowed
+  int32_t* row_map;      // [N] dense index m of a dense row, -1 for a sparse row
+  int32_t* sparse_rows;  // [N] the sparse rows, ascending
+  int32_t* n_sparse;     // [1]
+};
+
+// G2a: per-row OR of the tile flags, then an ascending numbering of the dense
+// rows (one workgroup, block prefix scan):  row_map, dense_rows[m] = n for
+// m < dense_cap, *n_dense = total, sparse_rows / *n_sparse, and *status =
+// OK / DENSE_CAPACITY.
+hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* dense_rows,
+                             int64_t dense_cap, int32_t* n_dense, int32_t* status, hipStream_t s);
 
 // G2b: dense_values[m] = row n of h (from `full_src` if given, else from the
 // TwELL slots of the row plus the spilled overflowing tiles), then the row's
@@ -58,10 +67,11 @@ hipError_t launch_unpack(const Geometry& g, int elem_bytes, const void* vals, co
                          const int32_t* n_dense, int64_t dense_cap, void* h, hipStream_t s);
 
 // G3: y[n] = sum of value * w_down[row] over the stored slots of row n, for
-// every row n (rows listed as dense in `row_map`, when given, are skipped).
+// the rows rows[0 .. *n_rows_dev) when `rows` is given, else for every row.
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
-                              const uint8_t* idx, const uint8_t* cnt, const int32_t* row_map,
-                              const void* w_down, void* y, hipStream_t s);
+                              const uint8_t* idx, const uint8_t* cnt, const int32_t* rows,
+                              const int32_t* n_rows_dev, const void* w_down, void* y,
+                              hipStream_t s);
 
 // G4: y[dense_rows[m]] = dense_values[m] w_down for m < min(*n_dense, dense_cap).
 hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,

@@ -55,20 +55,25 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// One thread per row: does any tile of the row overflow?
+__global__ __launch_bounds__(kRowThreads) void row_or_kernel(const uint8_t* __restrict__ flags,
+                                                             int64_t N, int nt,
+                                                             uint8_t* __restrict__ row_dense) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
+  if (n < N) row_dense[n] = row_has_flag(flags + n * nt, nt) ? 1 : 0;
+}
+
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
-    const uint8_t* __restrict__ flags, int64_t N, int nt, int32_t* __restrict__ row_map,
+    const uint8_t* __restrict__ row_dense, int64_t N, int32_t* __restrict__ row_map,
     int32_t* __restrict__ dense_rows, int64_t cap, int32_t* __restrict__ n_dense,
+    int32_t* __restrict__ sparse_rows, int32_t* __restrict__ n_sparse,
     int32_t* __restrict__ status) {
   __shared__ int wave_tot[kScanThreads / kWave];
   const int tid = threadIdx.x;
   const int64_t per = (N + kScanThreads - 1) / kScanThreads;
   const int64_t r0 = min(N, tid * per), r1 = min(N, r0 + per);
   int local = 0;
-  for (int64_t n = r0; n < r1; ++n) {
-    const bool d = row_has_flag(flags + n * nt, nt);
-    row_map[n] = d ? 1 : 0;  // re-read below by this same thread
-    local += d;
-  }
+  for (int64_t n = r0; n < r1; ++n) local += row_dense[n];
   const int incl = wave_inclusive_scan(local);
   const int wave = tid / kWave, lane = lane_id();
   if (lane == kWave - 1) wave_tot[wave] = incl;
@@ -78,18 +83,20 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
     before += (w < wave) ? wave_tot[w] : 0;
     total += wave_tot[w];
   }
-  int m = before + incl - local;  // exclusive prefix of this thread's rows
+  int m = before + incl - local;  // dense rows before this thread's first row
   for (int64_t n = r0; n < r1; ++n) {
-    if (row_map[n]) {
+    if (row_dense[n]) {
       row_map[n] = m;
       if (m < cap) dense_rows[m] = static_cast<int32_t>(n);
       ++m;
     } else {
       row_map[n] = -1;
+      sparse_rows[n - m] = static_cast<int32_t>(n);  // sparse rows before n = n - m
     }
   }
   if (tid == 0) {
     *n_dense = total;
+    *n_sparse = static_cast<int32_t>(N - total);
     if (status != nullptr) *status = total > cap ? TWELL_ERR_DENSE_CAPACITY : TWELL_OK;
   }
 }
@@ -123,35 +130,71 @@ __device__ __forceinline__ void gather_tile_vec(Vec16<E>& out, const E* __restri
   }
 }
 
-template <typename E>
+// One workgroup per row.  A dense row is assembled in LDS (zeros, then the
+// stored slots scattered in), then written out 16 bytes per thread, taking the
+// overflowing tiles from the spill area; with `full_src` the row is copied
+// from h as is.  Finally the row's TwELL slots are cleared.
+template <typename E, bool IN_LDS>
 __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
     int dff, int T, int C, int nt, const int32_t* __restrict__ row_map,
     const uint8_t* __restrict__ flags, const E* __restrict__ spill, const E* __restrict__ full_src,
     E* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
     E* __restrict__ dense_values, int64_t cap) {
   constexpr int V = Vec16<E>::N;
+  extern __shared__ __attribute__((aligned(16))) unsigned char mat_lds[];
+  E* rowbuf = reinterpret_cast<E*>(mat_lds);
   const int64_t n = blockIdx.x;
   const int m = row_map[n];
   if (m < 0) return;
   const int64_t slot0 = n * nt;
+  const int nslots = nt * C;
   if (m < cap) {
     E* dst = dense_values + static_cast<int64_t>(m) * dff;
-    for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
-      Vec16<E> o;
-      const int t = c / T;
-      if (full_src != nullptr) {
+    if (full_src != nullptr) {
+      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+        Vec16<E> o;
         load_vec(o, full_src + n * dff + c);
-      } else if (flags[slot0 + t]) {
-        load_vec(o, spill + n * dff + c);
-      } else {
-        const int64_t s = (slot0 + t) * C;
-        gather_tile_vec(o, vals + s, idx + s, cnt[slot0 + t], C, c - t * T);
+        store_vec(dst + c, o);
       }
-      store_vec(dst + c, o);
+    } else if (!IN_LDS) {  // row too long for LDS: rebuild each 16 bytes from the tile's slots
+      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+        Vec16<E> o;
+        const int t = c / T;
+        if (flags[slot0 + t]) {
+          load_vec(o, spill + n * dff + c);
+        } else {
+          const int64_t s = (slot0 + t) * C;
+          gather_tile_vec(o, vals + s, idx + s, cnt[slot0 + t], C, c - t * T);
+        }
+        store_vec(dst + c, o);
+      }
+    } else {
+      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+        Vec16<E> z;
+#pragma unroll
+        for (int i = 0; i < V; ++i) z.v[i] = E(0);
+        store_vec(rowbuf + c, z);
+      }
+      __syncthreads();
+      for (int s = threadIdx.x; s < nslots; s += kRowThreads) {
+        const int t = s / C;
+        if (s - t * C < static_cast<int>(cnt[slot0 + t])) {
+          const int local = idx[slot0 * C + s];
+          if (local < T) rowbuf[t * T + local] = vals[slot0 * C + s];
+        }
+      }
+      __syncthreads();
+      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+        Vec16<E> o;
+        if (flags[slot0 + c / T])
+          load_vec(o, spill + n * dff + c);
+        else
+          load_vec(o, rowbuf + c);
+        store_vec(dst + c, o);
+      }
     }
   }
   __syncthreads();  // every read of this row's slots is done before they are cleared
-  const int64_t nslots = static_cast<int64_t>(nt) * C;
   for (int64_t i = threadIdx.x; i < nslots; i += kRowThreads) {
     vals[slot0 * C + i] = E(0);
     idx[slot0 * C + i] = 0;
@@ -222,11 +265,15 @@ __global__ __launch_bounds__(kRowThreads) void unpack_kernel(
 
 }  // namespace
 
-hipError_t launch_route_scan(const Geometry& g, const uint8_t* flags, int32_t* row_map,
-                             int32_t* dense_rows, int64_t dense_cap, int32_t* n_dense,
-                             int32_t* status, hipStream_t s) {
-  route_scan_kernel<<<1, kScanThreads, 0, s>>>(flags, g.n_rows, g.n_tiles, row_map, dense_rows,
-                                               dense_cap, n_dense, status);
+hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* dense_rows,
+                             int64_t dense_cap, int32_t* n_dense, int32_t* status, hipStream_t s) {
+  if (g.n_rows > 0) {
+    const unsigned blocks = static_cast<unsigned>((g.n_rows + kRowThreads - 1) / kRowThreads);
+    row_or_kernel<<<blocks, kRowThreads, 0, s>>>(rb.flags, g.n_rows, g.n_tiles, rb.row_dense);
+  }
+  route_scan_kernel<<<1, kScanThreads, 0, s>>>(rb.row_dense, g.n_rows, rb.row_map, dense_rows,
+                                               dense_cap, n_dense, rb.sparse_rows, rb.n_sparse,
+                                               status);
   return hipGetLastError();
 }
 
@@ -236,13 +283,26 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
                               int64_t dense_cap, hipStream_t s) {
   if (g.n_rows == 0) return hipSuccess;
   const unsigned blocks = static_cast<unsigned>(g.n_rows);
-  if (elem_bytes == 2) {
-    materialize_kernel<uint16_t><<<blocks, kRowThreads, 0, s>>>(
+  const size_t row_bytes = static_cast<size_t>(g.d_ff) * elem_bytes;
+  const bool in_lds = full_src == nullptr && row_bytes <= 64 * 1024;
+  const size_t lds = in_lds ? row_bytes : 0;
+  if (elem_bytes == 2 && in_lds) {
+    materialize_kernel<uint16_t, true><<<blocks, kRowThreads, lds, s>>>(
+        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
+        static_cast<const uint16_t*>(spill), static_cast<const uint16_t*>(full_src),
+        static_cast<uint16_t*>(vals), idx, cnt, static_cast<uint16_t*>(dense_values), dense_cap);
+  } else if (elem_bytes == 4 && in_lds) {
+    materialize_kernel<float, true><<<blocks, kRowThreads, lds, s>>>(
+        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags, static_cast<const float*>(spill),
+        static_cast<const float*>(full_src), static_cast<float*>(vals), idx, cnt,
+        static_cast<float*>(dense_values), dense_cap);
+  } else if (elem_bytes == 2) {
+    materialize_kernel<uint16_t, false><<<blocks, kRowThreads, lds, s>>>(
         g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
         static_cast<const uint16_t*>(spill), static_cast<const uint16_t*>(full_src),
         static_cast<uint16_t*>(vals), idx, cnt, static_cast<uint16_t*>(dense_values), dense_cap);
   } else {
-    materialize_kernel<float><<<blocks, kRowThreads, 0, s>>>(
+    materialize_kernel<float, false><<<blocks, kRowThreads, lds, s>>>(
         g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags, static_cast<const float*>(spill),
         static_cast<const float*>(full_src), static_cast<float*>(vals), idx, cnt,
         static_cast<float*>(dense_values), dense_cap);

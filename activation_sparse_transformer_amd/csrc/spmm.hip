@@ -75,19 +75,21 @@ __device__ __forceinline__ uint4 store_form<float>(const float (&acc)[4]) {
 template <typename E>
 __global__ __launch_bounds__(kThreads) void spmm_sparse_kernel(
     const E* __restrict__ vals, const uint8_t* __restrict__ idx, const uint8_t* __restrict__ cnt,
-    const int32_t* __restrict__ row_map, const E* __restrict__ w, E* __restrict__ y, int64_t N,
-    int dm, int T, int C, int nt, int n_chunks) {
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_dev,
+    const E* __restrict__ w, E* __restrict__ y, int64_t N, int dm, int T, int C, int nt,
+    int n_chunks) {
   constexpr int V = SpmmVec<E>::N;
   typedef ElemTraits<E> Tr;
   const int lane = lane_id();
-  const int64_t items = N * n_chunks;
+  const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
+  const int64_t items = R * n_chunks;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
   const int nslots = nt * C;
   for (int64_t item = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + threadIdx.x / kWave;
        item < items; item += stride) {
-    const int chunk = static_cast<int>(item / N);
-    const int64_t n = item % N;
-    if (row_map != nullptr && row_map[n] >= 0) continue;  // dense row: the fallback GEMM writes it
+    const int chunk = static_cast<int>(item / R);
+    const int64_t k = item % R;
+    const int64_t n = rows != nullptr ? rows[k] : k;  // a listed (sparse) row, or every row
     const int col = chunk * (kWave * V) + lane * V;
     const bool live_col = col < dm;
     float acc[V];
@@ -202,9 +204,9 @@ constexpr int kListUnroll = 8;
 template <int VEC>
 __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
     const uint16_t* __restrict__ vals, const uint8_t* __restrict__ idx,
-    const uint8_t* __restrict__ cnt, const int32_t* __restrict__ row_map,
-    const uint16_t* __restrict__ w, uint16_t* __restrict__ y, int64_t N, int dm, int T, int C,
-    int nt, int n_slices) {
+    const uint8_t* __restrict__ cnt, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows_dev, const uint16_t* __restrict__ w,
+    uint16_t* __restrict__ y, int64_t N, int dm, int T, int C, int nt, int n_slices) {
   extern __shared__ uint2 spmm_lists[];
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int nslots = nt * C;
@@ -217,8 +219,9 @@ __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
   const int64_t wid = static_cast<int64_t>(blockIdx.x / 8) * kWavesPerBlock + wave;
   const int col = slice * (kWave * VEC) + lane * VEC;
   const char* wbase = reinterpret_cast<const char*>(w + col);
-  for (int64_t n = part + parts * wid; n < N; n += parts * per_xcd_waves) {
-    if (row_map != nullptr && row_map[n] >= 0) continue;  // dense row: the fallback GEMM writes it
+  const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
+  for (int64_t k = part + parts * wid; k < R; k += parts * per_xcd_waves) {
+    const int64_t n = rows != nullptr ? rows[k] : k;
     const int64_t s0 = n * nslots;
     int nnz = 0;
     for (int g = 0; g < nslots; g += kWave) {
@@ -275,8 +278,9 @@ __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
 }  // namespace
 
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
-                              const uint8_t* idx, const uint8_t* cnt, const int32_t* row_map,
-                              const void* w_down, void* y, hipStream_t s) {
+                              const uint8_t* idx, const uint8_t* cnt, const int32_t* rows,
+                              const int32_t* n_rows_dev, const void* w_down, void* y,
+                              hipStream_t s) {
   if (g.n_rows == 0) return hipSuccess;
   const int V = elem_bytes == 2 ? 8 : 4;
   const int n_chunks = (g.d_model + kWave * V - 1) / (kWave * V);
@@ -303,20 +307,20 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
       uint16_t* y16 = static_cast<uint16_t*>(y);
       if (vec == 8)
         spmm_list_bf16_kernel<8><<<xblocks, kThreads, list_bytes, s>>>(
-            v16, idx, cnt, row_map, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
+            v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
             n_slices);
       else
         spmm_list_bf16_kernel<16><<<xblocks, kThreads, list_bytes, s>>>(
-            v16, idx, cnt, row_map, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
+            v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
             n_slices);
       return hipGetLastError();
     }
     spmm_sparse_kernel<uint16_t><<<blocks, kThreads, 0, s>>>(
-        static_cast<const uint16_t*>(vals), idx, cnt, row_map, static_cast<const uint16_t*>(w_down),
+        static_cast<const uint16_t*>(vals), idx, cnt, rows, n_rows_dev, static_cast<const uint16_t*>(w_down),
         static_cast<uint16_t*>(y), g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles, n_chunks);
   } else {
     spmm_sparse_kernel<float><<<blocks, kThreads, 0, s>>>(
-        static_cast<const float*>(vals), idx, cnt, row_map, static_cast<const float*>(w_down),
+        static_cast<const float*>(vals), idx, cnt, rows, n_rows_dev, static_cast<const float*>(w_down),
         static_cast<float*>(y), g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles, n_chunks);
   }
   return hipGetLastError();

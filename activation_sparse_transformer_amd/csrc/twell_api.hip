@@ -56,14 +56,17 @@ Geometry geometry(const twell_shape* s) {
 }
 
 struct PackWorkspace {
-  uint8_t* flags;
-  int32_t* row_map;
+  RouteBufs route;
   void* spill;
 };
 
+// Workspace: flags [N][nt] u8 | row_dense [N] u8 | row_map [N] i32 |
+// sparse_rows [N] i32 | n_sparse i32 | (forward only) spill [N][d_ff] dtype,
+// each part 256-byte aligned.
 size_t pack_ws_bytes(const twell_shape* s) {
   const size_t n = static_cast<size_t>(s->n_rows);
-  return align_up(n * static_cast<size_t>(s->d_ff / s->tile)) + align_up(n * sizeof(int32_t));
+  return align_up(n * static_cast<size_t>(s->d_ff / s->tile)) + align_up(n) +
+         2 * align_up(n * sizeof(int32_t)) + align_up(sizeof(int32_t));
 }
 
 size_t fwd_ws_bytes(const twell_shape* s) {
@@ -75,10 +78,16 @@ PackWorkspace carve(const twell_shape* s, void* ws, bool with_spill) {
   PackWorkspace w;
   const size_t n = static_cast<size_t>(s->n_rows);
   uint8_t* p = static_cast<uint8_t*>(ws);
-  w.flags = p;
+  w.route.flags = p;
   p += align_up(n * static_cast<size_t>(s->d_ff / s->tile));
-  w.row_map = reinterpret_cast<int32_t*>(p);
+  w.route.row_dense = p;
+  p += align_up(n);
+  w.route.row_map = reinterpret_cast<int32_t*>(p);
   p += align_up(n * sizeof(int32_t));
+  w.route.sparse_rows = reinterpret_cast<int32_t*>(p);
+  p += align_up(n * sizeof(int32_t));
+  w.route.n_sparse = reinterpret_cast<int32_t*>(p);
+  p += align_up(sizeof(int32_t));
   w.spill = with_spill ? p : nullptr;
   return w;
 }
@@ -95,9 +104,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_ERR_HIP
 // the dense rows, sparse product, dense fallback.
 int route_and_materialize(const Geometry& g, int eb, const PackWorkspace& w, const void* full_src,
                           const twell_hybrid* hy, int32_t* d_status, hipStream_t st) {
-  TWELL_TRY(launch_route_scan(g, w.flags, w.row_map, hy->dense_rows, hy->dense_capacity,
-                              hy->n_dense, d_status, st));
-  TWELL_TRY(launch_materialize(g, eb, w.row_map, w.flags, w.spill, full_src, hy->values,
+  TWELL_TRY(launch_route_scan(g, w.route, hy->dense_rows, hy->dense_capacity, hy->n_dense,
+                              d_status, st));
+  TWELL_TRY(launch_materialize(g, eb, w.route.row_map, w.route.flags, w.spill, full_src, hy->values,
                                hy->indices, hy->counts, hy->dense_values, hy->dense_capacity, st));
   return TWELL_OK;
 }
@@ -164,7 +173,7 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
 
   TWELL_TRY(mark(0));
   // 1. up-projection + bias + ReLU with the TwELL pack in its epilogue
-  PackOut po{h_out->values, h_out->indices, h_out->counts, w.flags, w.spill, h_dense_debug};
+  PackOut po{h_out->values, h_out->indices, h_out->counts, w.route.flags, w.spill, h_dense_debug};
   if (g.n_rows > 0) {
     if (eb == 2)
       TWELL_TRY(launch_up_pack_bf16(g, static_cast<const uint16_t*>(x),
@@ -179,8 +188,8 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
   TWELL_TRY(mark(2));
   // 3. sparse down-projection of the TwELL rows
   if (g.n_rows > 0)
-    TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts, w.row_map,
-                                 w_down, y, st));
+    TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts,
+                                 w.route.sparse_rows, w.route.n_sparse, w_down, y, st));
   TWELL_TRY(mark(3));
   // 4. dense fallback for the dense rows
   if (g.n_rows > 0) {
@@ -235,7 +244,7 @@ TWELL_EXPORT int twell_pack(const twell_shape* shape, const void* h, const twell
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int eb = elem_bytes(shape->dtype);
   const PackWorkspace w = carve(shape, workspace, false);
-  PackOut po{out->values, out->indices, out->counts, w.flags, nullptr, nullptr};
+  PackOut po{out->values, out->indices, out->counts, w.route.flags, nullptr, nullptr};
   TWELL_TRY(launch_pack_tiles(g, h, eb, po, st));
   return route_and_materialize(g, eb, w, h, out, d_status, st);
 }
@@ -265,7 +274,8 @@ TWELL_EXPORT int twell_spmm(const twell_shape* shape, const twell_hybrid* in, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int eb = elem_bytes(shape->dtype);
   // every row from its TwELL slots (dense rows hold none and come out 0) ...
-  TWELL_TRY(launch_spmm_sparse(g, eb, in->values, in->indices, in->counts, nullptr, w_down, y, st));
+  TWELL_TRY(launch_spmm_sparse(g, eb, in->values, in->indices, in->counts, nullptr, nullptr,
+                               w_down, y, st));
   // ... then the stored dense rows are overwritten by the fallback GEMM
   if (eb == 2)
     TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(in->dense_values),

@@ -61,9 +61,11 @@ def test_version_and_status_strings(lib):
 def test_workspace_sizes(lib):
     s = twell.make_shape(4096, 2048, 8192, 128, 4, __import__("torch").bfloat16)
     ws = twell.ffn_workspace_bytes(s)
-    # flags [N, nt] + row map [N] int32 + spill [N, d_ff] bf16, each 256-aligned
-    assert ws == 4096 * 64 + 4096 * 4 + 4096 * 8192 * 2
-    assert twell.pack_workspace_bytes(s) == 4096 * 64 + 4096 * 4
+    # flags [N, nt] + row flags [N] + row map, sparse rows [N] int32 + a counter
+    # (+ spill [N, d_ff] bf16 for the forward), each part 256-byte aligned
+    route = 4096 * 64 + 4096 + 2 * 4096 * 4 + 256
+    assert twell.pack_workspace_bytes(s) == route
+    assert ws == route + 4096 * 8192 * 2
     bad = twell.make_shape(16, 2048, 8192, 100, 4, __import__("torch").bfloat16)
     assert twell.ffn_workspace_bytes(bad) == 0
 

@@ -149,6 +149,8 @@ SMALL = [
     ("ffn_1b_bf16", 150, 2048, 512),
     ("hybrid_stress_bf16", 40, 4096, 384),
     ("large_bf16", 24, 8192, 512),
+    # a float32 row longer than 64 KB: dense rows rebuilt without the LDS row buffer
+    ("tiny_fp32", 20, 64, 16448),
 ]
 
 
