@@ -178,10 +178,11 @@ __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
       __syncthreads();
       for (int s = threadIdx.x; s < nslots; s += kRowThreads) {
         const int t = s / C;
-        if (s - t * C < static_cast<int>(cnt[slot0 + t])) {
-          const int local = idx[slot0 * C + s];
-          if (local < T) rowbuf[t * T + local] = vals[slot0 * C + s];
-        }
+        // count, index and value loaded together: no load waits on another
+        const int count = cnt[slot0 + t];
+        const int local = idx[slot0 * C + s];
+        const E v = vals[slot0 * C + s];
+        if (s - t * C < count && local < T) rowbuf[t * T + local] = v;
       }
       __syncthreads();
       for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
