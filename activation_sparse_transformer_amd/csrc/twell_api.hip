@@ -4,6 +4,8 @@
 #include "../../include/twell.h"
 #include "kernels.h"
 
+#include <mutex>
+
 #define TWELL_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace twell {
@@ -94,6 +96,39 @@ PackWorkspace carve(const twell_shape* s, void* ws, bool with_spill) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_ERR_HIP; }
 
+// Per-device auxiliary stream on which the forward pass runs its sparse
+// product while the dense fallback runs on the caller's stream (the two
+// write disjoint rows of y).  Created on first use, default priority,
+// non-blocking; it and its two events live until the process ends.  The
+// mutex serialises the fork / join enqueue of concurrent host threads.
+struct AuxStream {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+constexpr int kMaxDevices = 64;
+AuxStream g_aux[kMaxDevices];
+
+AuxStream* aux_stream(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  AuxStream* a = &g_aux[dev];
+  std::call_once(a->once, [a] {
+    a->err = hipStreamCreateWithFlags(&a->stream, hipStreamNonBlocking);
+    if (a->err == hipSuccess) a->err = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming);
+    if (a->err == hipSuccess) a->err = hipEventCreateWithFlags(&a->join, hipEventDisableTiming);
+  });
+  *err = a->err;
+  return a->err == hipSuccess ? a : nullptr;
+}
+
 #define TWELL_TRY(expr)                          \
   do {                                           \
     const hipError_t e_ = (expr);                \
@@ -144,7 +179,8 @@ namespace twell {
 namespace {
 
 // The forward pass; `ev`, when given, holds five events recorded on the
-// stream before step 1 and after each of steps 1-4.
+// stream before step 1 and after each of steps 1-4 (which then run in
+// order on the stream).
 int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, const float* b_up,
                  const void* w_down, void* y, const twell_hybrid* h_out, void* h_dense_debug,
                  void* workspace, size_t workspace_bytes, int32_t* d_status, void* stream,
@@ -186,13 +222,26 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
   // 2. route rows, build dense rows from the TwELL slots + spilled tiles
   if ((rc = route_and_materialize(g, eb, w, nullptr, h_out, d_status, st)) != TWELL_OK) return rc;
   TWELL_TRY(mark(2));
-  // 3. sparse down-projection of the TwELL rows
-  if (g.n_rows > 0)
-    TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts,
-                                 w.route.sparse_rows, w.route.n_sparse, w_down, y, st));
-  TWELL_TRY(mark(3));
-  // 4. dense fallback for the dense rows
+  // 3. sparse down-projection of the TwELL rows and 4. dense fallback for the
+  // dense rows.  They write disjoint rows of y: the plain call runs 3 on the
+  // auxiliary stream concurrently with 4 on the caller's stream; the timed
+  // variant runs them one after the other so each stage can be timed alone.
   if (g.n_rows > 0) {
+    AuxStream* a = nullptr;
+    std::unique_lock<std::mutex> lock;
+    hipStream_t sp = st;
+    if (ev == nullptr) {
+      hipError_t e = hipSuccess;
+      a = aux_stream(&e);
+      TWELL_TRY(e);
+      lock = std::unique_lock<std::mutex>(a->mu);
+      TWELL_TRY(hipEventRecord(a->fork, st));
+      TWELL_TRY(hipStreamWaitEvent(a->stream, a->fork, 0));
+      sp = a->stream;
+    }
+    TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts,
+                                 w.route.sparse_rows, w.route.n_sparse, w_down, y, sp));
+    TWELL_TRY(mark(3));
     if (eb == 2)
       TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(h_out->dense_values),
                                      h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
@@ -203,6 +252,12 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
                                     h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
                                     static_cast<const float*>(w_down), static_cast<float*>(y),
                                     st));
+    if (a != nullptr) {
+      TWELL_TRY(hipEventRecord(a->join, a->stream));
+      TWELL_TRY(hipStreamWaitEvent(st, a->join, 0));
+    }
+  } else {
+    TWELL_TRY(mark(3));
   }
   TWELL_TRY(mark(4));
   return TWELL_OK;

@@ -75,9 +75,11 @@ def time_forward(cfg, d, bufs, steps, warmup, flush):
     """ffn_sparse_forward, cold cache.
 
     Two timed loops of `steps` each: the headline times whole plain calls with
-    an event pair around each; the breakdown uses ffn_sparse_forward_events,
-    whose extra event records on the stream add a few microseconds of gaps
-    between stages, so its total is not the headline.
+    an event pair around each (the sparse product then runs on the library's
+    auxiliary stream, concurrently with the dense fallback); the breakdown uses
+    ffn_sparse_forward_events, which runs the four stages one after the other
+    with events between them, so each stage is one kernel sequence timed
+    alone and its total is not the headline.
     """
     fwd = lambda **kw: twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"],
                                                 cfg.tile, cfg.capacity, out=bufs, **kw)

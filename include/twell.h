@@ -138,6 +138,12 @@ size_t ffn_sparse_workspace_size(const twell_shape* shape);
  *      of value * w_down[t*tile + index];
  *   4. dense fallback GEMM for the dense rows: y[dense_rows[m]] =
  *      dense_values[m] W_down.
+ * Steps 3 and 4 write disjoint rows of y and run concurrently: step 3 on a
+ * library-owned auxiliary stream of the current device (created on the first
+ * call, kept until the process ends), forked from and joined back into
+ * `stream` with events, so all work still completes in `stream` order and the
+ * pass can be captured into a HIP graph from `stream`.  Calls on one device
+ * share that auxiliary stream. 
  * Arguments: shape (host pointer); x, w_up_t, b_up, w_down inputs; y output;
  * h_out (host pointer to a struct of device pointers) receives h in hybrid
  * TwELL form; h_dense_debug, if non-NULL, receives h [n_rows][d_ff] exactly
@@ -156,8 +162,9 @@ int ffn_sparse_forward(const twell_shape* shape, const void* x, const void* w_up
 
 /* ffn_sparse_forward that also records five caller-created HIP events
  * (stage_events[0..4], hipEvent_t passed as void*) on `stream`: before step
- * 1 and after each of steps 1-4, so a caller can time every stage with
- * hipEventElapsedTime on the stream the kernels run on.  Same arguments,
+ * 1 and after each of steps 1-4.  Here steps 3 and 4 run one after the other
+ * on `stream` (no auxiliary stream), so a caller can time every stage alone
+ * with hipEventElapsedTime on the stream the kernels run on.  Same arguments,
  * results and errors as ffn_sparse_forward; a NULL array or event is
  * TWELL_ERR_INVALID_ARG. */
 int ffn_sparse_forward_events(const twell_shape* shape, const void* x, const void* w_up_t,

@@ -104,6 +104,29 @@ def test_spmm_integer_exact(dtype, n, dm, T, C):
     np.testing.assert_array_equal(as_f64(y), y_ref)
 
 
+@pytest.mark.parametrize("n,dm,dff,T,density", [
+    (4500, 512, 512, 128, 0.01),  # many row batches per wave of the XCD-sliced kernel
+    (400, 40, 9728, 128, 0.01),   # a long d_ff with a d_model the sliced kernel does not take
+    (128, 1024, 896, 64, 0.03),   # d_model of two XCD slices
+])
+def test_spmm_many_rows_integer_exact(n, dm, dff, T, density):
+    """Every row checked, with values whose products and sums are exact."""
+    say(f"spmm rows n={n} dm={dm} dff={dff} T={T}")
+    rng = np.random.default_rng(n + dff)
+    h = rng.integers(-2, 3, size=(n, dff)).astype(np.float32)
+    h[rng.random((n, dff)) >= density] = 0
+    w = rng.integers(-1, 2, size=(dff, dm)).astype(np.float32)
+    w[rng.random((dff, dm)) < 0.7] = 0
+    hy, _ = twell.twell_pack(torch.from_numpy(h).to(torch.bfloat16).cuda(), T, 4)
+    y = twell.twell_spmm(hy, torch.from_numpy(w).to(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    ref_h = assert_pack_matches(hy, h)
+    assert 0 < ref_h.n_dense < n
+    y_ref = oracle.spmm(ref_h, w.astype(np.float64))
+    assert np.max(np.abs(y_ref)) <= 256
+    np.testing.assert_array_equal(as_f64(y), y_ref)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_spmm_identity_is_unpack(dtype):
     ht, hh = sparse_h(9, 90, 256, 0.05, DT[dtype])
@@ -233,3 +256,24 @@ def test_forward_matches_standalone_pack_and_spmm():
     np.testing.assert_array_equal(u32(as_f32(out.hybrid.dense_values[:nd])),
                                   u32(as_f32(hy.dense_values[:nd])))
     np.testing.assert_array_equal(u32(as_f32(out.y)), u32(as_f32(y2)))
+
+
+def test_forward_timed_variant_matches_plain_call():
+    """The event-recording variant (steps 3 and 4 in order on the stream) and
+    the plain call (step 3 on the auxiliary stream, concurrent with step 4)
+    give the same y and hybrid, bit for bit."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=700, d_model=512, d_ff=2048)
+    t = make_inputs(cfg)
+    d = inputs_to_device(t)
+    a = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
+                                 cfg.capacity)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    b = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
+                                 cfg.capacity, stage_events=evs)
+    torch.cuda.synchronize()
+    assert 0 < a.hybrid.n_dense_host() < cfg.n_rows
+    np.testing.assert_array_equal(u32(as_f32(a.y)), u32(as_f32(b.y)))
+    np.testing.assert_array_equal(a.hybrid.counts.cpu().numpy(), b.hybrid.counts.cpu().numpy())
+    assert all(evs[i].elapsed_time(evs[i + 1]) >= 0 for i in range(4))
+    _, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    assert_close_rel(as_f64(a.y), y_ref, TOL[cfg.torch_dtype], "y")
