@@ -569,7 +569,8 @@ __device__ __forceinline__ void up_pack_epilogue32(
     uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
     uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
   constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32, BM = CF::BM;
-  static_assert(CF::WTN == 64 && FN == 2 && CF::WAVES_N == 4, "64-column segments, 4 per row");
+  constexpr int SPW = CF::WTN / 64;  // 64-column segments per wave
+  static_assert(CF::WTN % 64 == 0 && CF::BN / 64 <= 4, "whole segments, at most 4 per block row");
   typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
   typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
   // LDS: per-(row, segment) counts, then (staged) slot values, indices, counts, flags
@@ -581,18 +582,26 @@ __device__ __forceinline__ void up_pack_epilogue32(
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
   const int hh = lane >> 5, c = lane & 31;
-  const int seg_col = n0 + wn * 64;   // first column of this wave's segment
-  const bool seg_ok = seg_col < N;    // segments (and tiles) are all-in or all-out
-  const int spt = T / 64;             // segments per tile
-  const int first = wn & ~(spt - 1);  // first segment of this wave's tile
-  const int t = seg_col / T;          // global tile index
-  const int tb = (wn * 64) / T;       // tile index inside the block
-  const int tpb = CF::BN / T;         // tiles per block
+  const int spt = T / 64;  // segments per tile
   const uint32_t below = (1u << c) - 1u;
-  // byte masks selecting the tile's segments, and those left of this wave
-  const uint32_t tile_mask = (spt == 4 ? 0x01010101u : spt == 2 ? 0x0101u : 0x01u) << (8 * first);
-  const int nleft = wn - first;        // segments of the tile left of this wave (0..3)
-  const uint32_t left_mask = nleft == 0 ? 0u : (0x01010101u >> (8 * (4 - nleft))) << (8 * first);
+  // per segment sj of this wave (block segment sg = wn * SPW + sj)
+  int seg_col[SPW], first[SPW], t[SPW], tb[SPW];
+  bool seg_ok[SPW];
+  uint32_t tile_mask[SPW], left_mask[SPW];
+#pragma unroll
+  for (int sj = 0; sj < SPW; ++sj) {
+    const int sg = wn * SPW + sj;
+    seg_col[sj] = n0 + sg * 64;   // first column of the segment
+    seg_ok[sj] = seg_col[sj] < N;  // segments (and tiles) are all-in or all-out
+    first[sj] = sg & ~(spt - 1);   // first segment of the segment's tile
+    t[sj] = seg_col[sj] / T;       // global tile index
+    tb[sj] = (sg * 64) / T;        // tile index inside the block
+    // byte masks selecting the tile's segments, and those left of this one
+    tile_mask[sj] = (spt == 4 ? 0x01010101u : spt == 2 ? 0x0101u : 0x01u) << (8 * first[sj]);
+    const int nleft = sg - first[sj];
+    left_mask[sj] = nleft == 0 ? 0u : (0x01010101u >> (8 * (4 - nleft))) << (8 * first[sj]);
+  }
+  const int tpb = CF::BN / T;  // tiles per block
   if constexpr (STAGED) {
     for (int e = threadIdx.x; e < BM * kStagedSlots / 2; e += CF::NT) {
       reinterpret_cast<uint32_t*>(sv)[e] = 0u;
@@ -602,18 +611,19 @@ __device__ __forceinline__ void up_pack_epilogue32(
   float bj[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int col = seg_col + j * 32 + c;
+    const int col = n0 + wn * CF::WTN + j * 32 + c;
     bj[j] = col < N ? bias[col] : 0.f;
   }
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  // One 32-row block of the wave's rows; called with constant i below, so the
+  // accumulators are only ever indexed statically (no scratch copy).
+  auto block = [&](const int i, const fast::f32x16_t (&ai)[FN]) __attribute__((always_inline)) {
     // 1. h = ReLU(acc + b) as bf16 (+0.0 when off), two rows per register, RNE
     uint32_t hp[FN][8];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float z0 = acc[i][j][r] + bj[j], z1 = acc[i][j][r + 1] + bj[j];
+        const float z0 = ai[j][r] + bj[j], z1 = ai[j][r + 1] + bj[j];
         const f32x2_t z = {z0 > 0.f ? z0 : 0.f, z1 > 0.f ? z1 : 0.f};
         hp[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2_t));
       }
@@ -623,72 +633,84 @@ __device__ __forceinline__ void up_pack_epilogue32(
     auto half = [&](uint64_t m) -> uint32_t {
       return hh ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
     };
-    // 2. non-zero pattern per (row, segment); counts to LDS
-    uint32_t c0[16], c1[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      c0[r] = half(wave_ballot(hv(0, r) != 0u));
-      c1[r] = half(wave_ballot(hv(1, r) != 0u));
-    }
+    // 2. non-zero count per (row, segment) to LDS: the two ballots of a
+    // segment's 32-column halves, counted per 32-lane half of the wave (one
+    // row each); lane 0 posts the first row, lane 32 the second
     const int rl0 = wm * CF::WTM + i * 32 + hh * 4;  // row of register r = rl0 + (r/4)*8 + r%4
-    if (c == 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        seg[(rl0 + (r >> 2) * 8 + (r & 3)) * 4 + wn] = static_cast<uint8_t>(__popc(c0[r]) + __popc(c1[r]));
-    }
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int sj = 0; sj < SPW; ++sj) {
+        const uint64_t b0 = wave_ballot(hv(2 * sj, r) != 0u);
+        const uint64_t b1 = wave_ballot(hv(2 * sj + 1, r) != 0u);
+        const int lo = __popc(static_cast<uint32_t>(b0)) + __popc(static_cast<uint32_t>(b1));
+        const int hi = __popc(static_cast<uint32_t>(b0 >> 32)) + __popc(static_cast<uint32_t>(b1 >> 32));
+        if (c == 0)
+          seg[(rl0 + (r >> 2) * 8 + (r & 3)) * 4 + wn * SPW + sj] = static_cast<uint8_t>(hh ? hi : lo);
+      }
     __syncthreads();
-    // 3. slots, metadata, spill
+    // 3. slots, metadata, spill (the ballots are taken again: cheaper than
+    // keeping them live across the barrier)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int rl = rl0 + (r >> 2) * 8 + (r & 3);
       const int n = m0 + rl;
       const uint32_t counts = *reinterpret_cast<const uint32_t*>(seg + rl * 4);
-      const int total = static_cast<int>(__builtin_amdgcn_udot4(counts, tile_mask, 0u, false));
-      const int left = static_cast<int>(__builtin_amdgcn_udot4(counts, left_mask, 0u, false));
-      const bool fits = total <= C;
-      const bool row_ok = seg_ok && n < M;
-      const int pos0 = left;
-      const int pos1 = left + __popc(c0[r]);
-      const int64_t slot0 = (static_cast<int64_t>(n) * nt + t) * C;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t v = hv(j, r);
-        const int col = seg_col + j * 32 + c;
-        if (row_ok && v != 0u && fits) {
-          const int pos = (j ? pos1 : pos0) + __popc((j ? c1[r] : c0[r]) & below);
-          if constexpr (STAGED) {
-            sv[rl * kStagedSlots + tb * C + pos] = static_cast<uint16_t>(v);
-            si[rl * kStagedSlots + tb * C + pos] = static_cast<uint8_t>(col - t * T);
-          } else {
-            vals[slot0 + pos] = static_cast<uint16_t>(v);
-            idx[slot0 + pos] = static_cast<uint8_t>(col - t * T);
-          }
-        }
-        if (row_ok && !fits && spill != nullptr)
-          spill[static_cast<int64_t>(n) * N + col] = static_cast<uint16_t>(v);
-        if (row_ok && hdebug != nullptr)
-          hdebug[static_cast<int64_t>(n) * N + col] = static_cast<uint16_t>(v);
-      }
-      if (row_ok && wn == first) {
-        if constexpr (STAGED) {
-          if (c == 0) {
-            sc[rl * 4 + tb] = static_cast<uint8_t>(fits ? total : 0);
-            sf[rl * 4 + tb] = static_cast<uint8_t>(fits ? 0 : 1);
-          }
-        } else {
-          if (c == 0) {
-            cnt[static_cast<int64_t>(n) * nt + t] = static_cast<uint8_t>(fits ? total : 0);
-            flags[static_cast<int64_t>(n) * nt + t] = static_cast<uint8_t>(fits ? 0 : 1);
-          }
-          if (fits)
-            for (int sl = total + c; sl < C; sl += 32) {
-              vals[slot0 + sl] = 0;
-              idx[slot0 + sl] = 0;
+      for (int sj = 0; sj < SPW; ++sj) {
+        const int total = static_cast<int>(__builtin_amdgcn_udot4(counts, tile_mask[sj], 0u, false));
+        const int left = static_cast<int>(__builtin_amdgcn_udot4(counts, left_mask[sj], 0u, false));
+        const bool fits = total <= C;
+        const bool row_ok = seg_ok[sj] && n < M;
+        const int64_t slot0 = (static_cast<int64_t>(n) * nt + t[sj]) * C;
+        const uint32_t cm0 = half(wave_ballot(hv(2 * sj, r) != 0u));
+        const uint32_t cm1 = half(wave_ballot(hv(2 * sj + 1, r) != 0u));
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int j = 2 * sj + h2;
+          const uint32_t v = hv(j, r);
+          const int col = seg_col[sj] + h2 * 32 + c;
+          if (row_ok && v != 0u && fits) {
+            const int pos = left + (h2 ? __popc(cm0) : 0) + __popc((h2 ? cm1 : cm0) & below);
+            if constexpr (STAGED) {
+              sv[rl * kStagedSlots + tb[sj] * C + pos] = static_cast<uint16_t>(v);
+              si[rl * kStagedSlots + tb[sj] * C + pos] = static_cast<uint8_t>(col - t[sj] * T);
+            } else {
+              vals[slot0 + pos] = static_cast<uint16_t>(v);
+              idx[slot0 + pos] = static_cast<uint8_t>(col - t[sj] * T);
             }
+          }
+          if (row_ok && !fits && spill != nullptr)
+            spill[static_cast<int64_t>(n) * N + col] = static_cast<uint16_t>(v);
+          if (row_ok && hdebug != nullptr)
+            hdebug[static_cast<int64_t>(n) * N + col] = static_cast<uint16_t>(v);
+        }
+        if (row_ok && wn * SPW + sj == first[sj]) {
+          if constexpr (STAGED) {
+            if (c == 0) {
+              sc[rl * 4 + tb[sj]] = static_cast<uint8_t>(fits ? total : 0);
+              sf[rl * 4 + tb[sj]] = static_cast<uint8_t>(fits ? 0 : 1);
+            }
+          } else {
+            if (c == 0) {
+              cnt[static_cast<int64_t>(n) * nt + t[sj]] = static_cast<uint8_t>(fits ? total : 0);
+              flags[static_cast<int64_t>(n) * nt + t[sj]] = static_cast<uint8_t>(fits ? 0 : 1);
+            }
+            if (fits)
+              for (int sl = total + c; sl < C; sl += 32) {
+                vals[slot0 + sl] = 0;
+                idx[slot0 + sl] = 0;
+              }
+          }
         }
       }
     }
-  }
+  };
+  static_assert(FM <= 4, "up to four 32-row blocks per wave");
+  block(0, acc[0]);
+  if constexpr (FM > 1) block(1, acc[1]);
+  if constexpr (FM > 2) block(2, acc[2]);
+  if constexpr (FM > 3) block(3, acc[3]);
   if constexpr (STAGED) {
     __syncthreads();
     // copy the block's slots out: each row owns one contiguous run per array
@@ -807,6 +829,9 @@ __global__ __launch_bounds__(CF::NT) void fallback_bf16_fast(
     }
 }
 
+// G1: 256 x 256 blocks, 8 waves of 128 x 64 (2 waves per SIMD hide each
+// other's LDS waits; 4 waves of 128 x 128 halve the LDS reads per MFMA but
+// measured 1.45x slower at one wave per SIMD).
 typedef fast::Cfg<256, 256, 2, 4> BigCfg;
 typedef fast::Cfg<128, 128, 2, 4> MidCfg;
 
