@@ -258,11 +258,12 @@ def test_forward_matches_standalone_pack_and_spmm():
     np.testing.assert_array_equal(u32(as_f32(out.y)), u32(as_f32(y2)))
 
 
-def test_forward_timed_variant_matches_plain_call():
-    """The event-recording variant (steps 3 and 4 in order on the stream) and
-    the plain call (step 3 on the auxiliary stream, concurrent with step 4)
-    give the same y and hybrid, bit for bit."""
-    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=700, d_model=512, d_ff=2048)
+@pytest.mark.parametrize("n_rows", [700, 1500, 2600])
+def test_forward_timed_variant_matches_plain_call(n_rows):
+    """The event-recording variant (every stage in order on the stream) and the
+    plain call (sparse product on the auxiliary stream, concurrent with the
+    fallback) give the same y and hybrid, bit for bit."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=512, d_ff=2048)
     t = make_inputs(cfg)
     d = inputs_to_device(t)
     a = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
@@ -274,6 +275,14 @@ def test_forward_timed_variant_matches_plain_call():
     assert 0 < a.hybrid.n_dense_host() < cfg.n_rows
     np.testing.assert_array_equal(u32(as_f32(a.y)), u32(as_f32(b.y)))
     np.testing.assert_array_equal(a.hybrid.counts.cpu().numpy(), b.hybrid.counts.cpu().numpy())
+    np.testing.assert_array_equal(a.hybrid.indices.cpu().numpy(), b.hybrid.indices.cpu().numpy())
+    np.testing.assert_array_equal(u32(as_f32(a.hybrid.values)), u32(as_f32(b.hybrid.values)))
+    nd = a.hybrid.n_dense_host()
+    assert nd == b.hybrid.n_dense_host()
+    np.testing.assert_array_equal(a.hybrid.dense_rows[:nd].cpu().numpy(),
+                                  b.hybrid.dense_rows[:nd].cpu().numpy())
+    np.testing.assert_array_equal(u32(as_f32(a.hybrid.dense_values[:nd])),
+                                  u32(as_f32(b.hybrid.dense_values[:nd])))
     assert all(evs[i].elapsed_time(evs[i + 1]) >= 0 for i in range(4))
     _, y_ref = oracle.ffn_forward(*oracle_inputs(t))
     assert_close_rel(as_f64(a.y), y_ref, TOL[cfg.torch_dtype], "y")
