@@ -829,6 +829,97 @@ __global__ __launch_bounds__(CF::NT) void fallback_bf16_fast(
     }
 }
 
+// ------------------------------------------------- skinny split-K (bf16, <= 64 rows)
+// Workgroup (column block, slice) runs the DMA + MFMA main loop over its K
+// slice only and stores fp32 partial sums part[slice][m][n] (row stride mm)
+// for the live rows; the slice sums and epilogues are shared with the fp32
+// skinny kernels.  A has at most 64 rows, so each weight tile is used for one
+// MFMA row block and the pair is bound by streaming the weight from HBM.
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void skinny_up_partial_bf16(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_up_t, int M, int N, int K,
+    int kw, int mm, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+  const int n0 = blockIdx.x * CF::BN, slice = blockIdx.y, kbeg = slice * kw;
+  fast::f32x16_t acc[CF::WTM / 32][CF::WTN / 32];
+  fast::mainloop32<CF>(x + kbeg, K, M, 0, w_up_t + kbeg, K, N, n0, min(kw, K - kbeg), lds, acc);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  float* dst = part + static_cast<int64_t>(slice) * mm * N;
+#pragma unroll
+  for (int i = 0; i < CF::WTM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < CF::WTN / 32; ++j) {
+      const int col = n0 + wn * CF::WTN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm * CF::WTM + i * 32 + (r / 4) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < M && col < N) dst[static_cast<int64_t>(m) * N + col] = acc[i][j][r];
+      }
+    }
+}
+
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void skinny_fallback_partial_bf16(
+    const uint16_t* __restrict__ dense_values, const int32_t* __restrict__ n_dense, int m_cap,
+    const uint16_t* __restrict__ w_down, int N, int K, int kw, int mm, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+  const int M = min(*n_dense, m_cap);
+  if (M <= 0) return;
+  const int n0 = blockIdx.x * CF::BN, slice = blockIdx.y, kbeg = slice * kw;
+  f32x4_t acc[CF::FM][CF::FN];
+  fast::mainloop_kn<CF>(dense_values + kbeg, K, M, 0, w_down + static_cast<int64_t>(kbeg) * N, N,
+                        N, n0, min(kw, K - kbeg), lds, acc);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  float* dst = part + static_cast<int64_t>(slice) * mm * N;
+#pragma unroll
+  for (int i = 0; i < CF::FM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = wm * CF::WTM + i * 16 + (lane >> 4) * 4 + r;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < CF::FN; ++j) {
+        const int col = n0 + wn * CF::WTN + j * 16 + (lane & 15);
+        if (col < N) dst[static_cast<int64_t>(m) * N + col] = acc[i][j][r];
+      }
+    }
+}
+
+// 32 rows x 128 columns (4 waves side by side) or 64 x 128 (2 x 2 waves):
+// 40-48 KB of LDS, three workgroups per CU.
+typedef fast::Cfg<32, 128, 1, 4> SkinnyCfg32;
+typedef fast::Cfg<64, 128, 2, 2> SkinnyCfg64;
+constexpr int kSkinnyTargetBlocks = 768;
+
+template <class CF>
+hipError_t skinny_up_bf16(const Geometry& g, const uint16_t* x, const uint16_t* w_up_t,
+                          const float* b_up, const PackOut& out, hipStream_t s) {
+  const int N = g.d_ff, K = g.d_model;
+  const int nb = (N + CF::BN - 1) / CF::BN;
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb, fast::BKF, kSkinnyTargetBlocks);
+  skinny_up_partial_bf16<CF><<<dim3(nb, sp.slices), CF::NT, 0, s>>>(
+      x, w_up_t, static_cast<int>(g.n_rows), N, K, sp.kw, sp.mm, out.skinny);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_skinny_up_epilogue<uint16_t>(g, sp, out.skinny, b_up, out, s);
+}
+
+template <class CF>
+hipError_t skinny_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
+                                const int32_t* dense_rows, const int32_t* n_dense, int m_cap,
+                                const uint16_t* w_down, uint16_t* y, float* part, hipStream_t s) {
+  const int N = g.d_model, K = g.d_ff;
+  const int nb = (N + CF::BN - 1) / CF::BN;
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb, fast::BKF, kSkinnyTargetBlocks);
+  skinny_fallback_partial_bf16<CF><<<dim3(nb, sp.slices), CF::NT, 0, s>>>(
+      dense_values, n_dense, m_cap, w_down, N, K, sp.kw, sp.mm, part);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_skinny_fallback_reduce<uint16_t>(g, sp, part, n_dense, m_cap, dense_rows, y, s);
+}
+
 // G1: 256 x 256 blocks, 8 waves of 128 x 64 (2 waves per SIMD hide each
 // other's LDS waits; 4 waves of 128 x 128 halve the LDS reads per MFMA but
 // measured 1.45x slower at one wave per SIMD).
@@ -839,6 +930,9 @@ typedef fast::Cfg<128, 128, 2, 4> MidCfg;
 
 hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint16_t* w_up_t,
                                const float* b_up, const PackOut& out, hipStream_t s) {
+  if (out.skinny != nullptr && g.n_rows > 0 && g.n_rows <= kSkinnyMaxRows && g.d_model % 64 == 0)
+    return g.n_rows <= 32 ? skinny_up_bf16<SkinnyCfg32>(g, x, w_up_t, b_up, out, s)
+                          : skinny_up_bf16<SkinnyCfg64>(g, x, w_up_t, b_up, out, s);
   const int M = static_cast<int>(g.n_rows), N = g.d_ff, K = g.d_model;
   if (M == 0) return hipSuccess;
   auto* vals = static_cast<uint16_t*>(out.vals);
@@ -868,9 +962,16 @@ hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint1
 hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
                                 const int32_t* dense_rows, const int32_t* n_dense,
                                 int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
-                                hipStream_t s) {
+                                hipStream_t s, float* skinny) {
   const int64_t worst = dense_cap < g.n_rows ? dense_cap : g.n_rows;
   if (worst <= 0) return hipSuccess;
+  if (skinny != nullptr && g.n_rows <= kSkinnyMaxRows && g.d_ff % 64 == 0) {
+    const int m_cap = static_cast<int>(worst);
+    return g.n_rows <= 32 ? skinny_fallback_bf16<SkinnyCfg32>(g, dense_values, dense_rows, n_dense,
+                                                             m_cap, w_down, y, skinny, s)
+                          : skinny_fallback_bf16<SkinnyCfg64>(g, dense_values, dense_rows, n_dense,
+                                                             m_cap, w_down, y, skinny, s);
+  }
   const int N = g.d_model, K = g.d_ff;
   if (worst >= 128 && K % 64 == 0 && N >= 128) {
     const int64_t blocks =

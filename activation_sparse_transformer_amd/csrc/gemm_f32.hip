@@ -166,6 +166,8 @@ __global__ __launch_bounds__(kThreads) void fallback_f32_kernel(
 
 hipError_t launch_up_pack_f32(const Geometry& g, const float* x, const float* w_up_t,
                               const float* b_up, const PackOut& out, hipStream_t s) {
+  if (out.skinny != nullptr && g.n_rows <= kSkinnyMaxRows)
+    return launch_skinny_up_pack_f32(g, x, w_up_t, b_up, out, out.skinny, s);
   const int M = static_cast<int>(g.n_rows), N = g.d_ff, K = g.d_model;
   if (M == 0) return hipSuccess;
   const int blocks = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -177,9 +179,13 @@ hipError_t launch_up_pack_f32(const Geometry& g, const float* x, const float* w_
 
 hipError_t launch_fallback_f32(const Geometry& g, const float* dense_values,
                                const int32_t* dense_rows, const int32_t* n_dense,
-                               int64_t dense_cap, const float* w_down, float* y, hipStream_t s) {
+                               int64_t dense_cap, const float* w_down, float* y, hipStream_t s,
+                               float* skinny) {
   const int64_t worst = dense_cap < g.n_rows ? dense_cap : g.n_rows;
   if (worst <= 0) return hipSuccess;
+  if (skinny != nullptr && g.n_rows <= kSkinnyMaxRows)
+    return launch_skinny_fallback_f32(g, dense_values, dense_rows, n_dense, dense_cap, w_down, y,
+                                      skinny, s);
   const int N = g.d_model, K = g.d_ff;
   const int64_t blocks = ((worst + BM - 1) / BM) * ((N + BN - 1) / BN);
   fallback_f32_kernel<<<static_cast<int>(blocks), kThreads, 0, s>>>(dense_values, dense_rows,

@@ -16,6 +16,7 @@ struct PackOut {
   uint8_t* flags;    // [N][nt] workspace: 1 when the tile overflowed
   void* spill;       // [N][d_ff] workspace or nullptr: raw h of overflowing tiles
   void* h_debug;     // [N][d_ff] or nullptr: every h element as packed
+  float* skinny;     // skinny_ws_bytes(g) of workspace, or nullptr
 };
 
 struct Geometry {
@@ -26,6 +27,37 @@ struct Geometry {
   int capacity;
   int n_tiles;
 };
+
+// Batches of at most kSkinnyMaxRows rows take split-K "skinny" kernels for
+// the up-projection and the fallback when the caller passes skinny_ws_bytes(g)
+// of workspace (0 for larger batches): workgroup (column block, slice) writes
+// fp32 partial sums part[slice][m][n] (row stride mm), and a second kernel adds
+// the slices in slice order and applies the epilogue.
+constexpr int64_t kSkinnyMaxRows = 64;
+constexpr int kSkinnyMaxSlices = 32;
+struct SkinnySplit {
+  int slices;  // K slices (<= kSkinnyMaxSlices)
+  int kw;      // K per slice, a multiple of the kernel's granule; the last may be shorter
+  int mm;      // rows per slice block of the partials: 16, 32 or 64
+};
+// Enough slices for about target_blocks workgroups over n_blocks column blocks.
+SkinnySplit skinny_split(int64_t n_rows, int K, int n_blocks, int granule, int target_blocks);
+size_t skinny_ws_bytes(const Geometry& g);
+// fp32 inputs: VALU partial kernels.
+hipError_t launch_skinny_up_pack_f32(const Geometry& g, const float* x, const float* w_up_t,
+                                     const float* b_up, const PackOut& out, float* part,
+                                     hipStream_t s);
+hipError_t launch_skinny_fallback_f32(const Geometry& g, const float* a, const int32_t* dense_rows,
+                                      const int32_t* n_dense, int64_t dense_cap,
+                                      const float* w_down, float* y, float* part, hipStream_t s);
+// Second halves, shared with the bf16 MFMA partial kernels.
+template <typename E>
+hipError_t launch_skinny_up_epilogue(const Geometry& g, const SkinnySplit& sp, const float* part,
+                                     const float* b_up, const PackOut& out, hipStream_t s);
+template <typename E>
+hipError_t launch_skinny_fallback_reduce(const Geometry& g, const SkinnySplit& sp,
+                                         const float* part, const int32_t* n_dense, int m_cap,
+                                         const int32_t* dense_rows, E* y, hipStream_t s);
 
 // G1: h = ReLU(x w_up_t^T + b) rounded to dtype, packed per (row, tile).
 hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint16_t* w_up_t,
@@ -74,12 +106,14 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
                               hipStream_t s);
 
 // G4: y[dense_rows[m]] = dense_values[m] w_down for m < min(*n_dense, dense_cap).
+// `skinny`: skinny_ws_bytes(g) of workspace for the split-K path, or nullptr.
 hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
                                 const int32_t* dense_rows, const int32_t* n_dense,
                                 int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
-                                hipStream_t s);
+                                hipStream_t s, float* skinny = nullptr);
 hipError_t launch_fallback_f32(const Geometry& g, const float* dense_values,
                                const int32_t* dense_rows, const int32_t* n_dense,
-                               int64_t dense_cap, const float* w_down, float* y, hipStream_t s);
+                               int64_t dense_cap, const float* w_down, float* y, hipStream_t s,
+                               float* skinny = nullptr);
 
 }  // namespace twell

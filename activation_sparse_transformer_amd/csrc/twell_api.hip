@@ -60,11 +60,13 @@ Geometry geometry(const twell_shape* s) {
 struct PackWorkspace {
   RouteBufs route;
   void* spill;
+  float* skinny;  // split-K partial sums for batches of few rows, or nullptr
 };
 
 // Workspace: flags [N][nt] u8 | row_dense [N] u8 | row_map [N] i32 |
-// sparse_rows [N] i32 | n_sparse i32 | (forward only) spill [N][d_ff] dtype,
-// each part 256-byte aligned.
+// sparse_rows [N] i32 | n_sparse i32 | (forward only) spill [N][d_ff] dtype |
+// (forward only, at most 64 rows) split-K partial sums, each part 256-byte
+// aligned.
 size_t pack_ws_bytes(const twell_shape* s) {
   const size_t n = static_cast<size_t>(s->n_rows);
   return align_up(n * static_cast<size_t>(s->d_ff / s->tile)) + align_up(n) +
@@ -73,7 +75,8 @@ size_t pack_ws_bytes(const twell_shape* s) {
 
 size_t fwd_ws_bytes(const twell_shape* s) {
   const size_t n = static_cast<size_t>(s->n_rows);
-  return pack_ws_bytes(s) + align_up(n * static_cast<size_t>(s->d_ff) * elem_bytes(s->dtype));
+  return pack_ws_bytes(s) + align_up(n * static_cast<size_t>(s->d_ff) * elem_bytes(s->dtype)) +
+         align_up(skinny_ws_bytes(geometry(s)));
 }
 
 PackWorkspace carve(const twell_shape* s, void* ws, bool with_spill) {
@@ -91,6 +94,11 @@ PackWorkspace carve(const twell_shape* s, void* ws, bool with_spill) {
   w.route.n_sparse = reinterpret_cast<int32_t*>(p);
   p += align_up(sizeof(int32_t));
   w.spill = with_spill ? p : nullptr;
+  w.skinny = nullptr;
+  if (with_spill) {
+    p += align_up(n * static_cast<size_t>(s->d_ff) * elem_bytes(s->dtype));
+    if (skinny_ws_bytes(geometry(s)) > 0) w.skinny = reinterpret_cast<float*>(p);
+  }
   return w;
 }
 
@@ -209,7 +217,8 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
 
   TWELL_TRY(mark(0));
   // 1. up-projection + bias + ReLU with the TwELL pack in its epilogue
-  PackOut po{h_out->values, h_out->indices, h_out->counts, w.route.flags, w.spill, h_dense_debug};
+  PackOut po{h_out->values, h_out->indices, h_out->counts, w.route.flags, w.spill, h_dense_debug,
+             w.skinny};
   if (g.n_rows > 0) {
     if (eb == 2)
       TWELL_TRY(launch_up_pack_bf16(g, static_cast<const uint16_t*>(x),
@@ -246,12 +255,12 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
       TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(h_out->dense_values),
                                      h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
                                      static_cast<const uint16_t*>(w_down),
-                                     static_cast<uint16_t*>(y), st));
+                                     static_cast<uint16_t*>(y), st, w.skinny));
     else
       TWELL_TRY(launch_fallback_f32(g, static_cast<const float*>(h_out->dense_values),
                                     h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
                                     static_cast<const float*>(w_down), static_cast<float*>(y),
-                                    st));
+                                    st, w.skinny));
     if (a != nullptr) {
       TWELL_TRY(hipEventRecord(a->join, a->stream));
       TWELL_TRY(hipStreamWaitEvent(st, a->join, 0));
@@ -299,7 +308,7 @@ TWELL_EXPORT int twell_pack(const twell_shape* shape, const void* h, const twell
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int eb = elem_bytes(shape->dtype);
   const PackWorkspace w = carve(shape, workspace, false);
-  PackOut po{out->values, out->indices, out->counts, w.route.flags, nullptr, nullptr};
+  PackOut po{out->values, out->indices, out->counts, w.route.flags, nullptr, nullptr, nullptr};
   TWELL_TRY(launch_pack_tiles(g, h, eb, po, st));
   return route_and_materialize(g, eb, w, h, out, d_status, st);
 }

@@ -66,6 +66,17 @@ def test_workspace_sizes(lib):
     route = 4096 * 64 + 4096 + 2 * 4096 * 4 + 256
     assert twell.pack_workspace_bytes(s) == route
     assert ws == route + 4096 * 8192 * 2
+    # at most 64 rows: split-K partial sums too, fp32 [up to 32 K slices][16/32/64 rows]
+    # [the wider of d_ff and d_model]
+    d = twell.make_shape(16, 4096, 16384, 128, 4, __import__("torch").bfloat16)
+    pack = 2048 + 256 + 2 * 256 + 256
+    spill = 16 * 16384 * 2
+    partials = 32 * 16 * 16384 * 4
+    assert twell.pack_workspace_bytes(d) == pack
+    assert twell.ffn_workspace_bytes(d) == pack + spill + partials
+    t = twell.make_shape(40, 136, 768, 128, 4, __import__("torch").bfloat16)  # 32 < 40 <= 64 rows
+    partials = 32 * 64 * 768 * 4
+    assert twell.ffn_workspace_bytes(t) == twell.pack_workspace_bytes(t) + 40 * 768 * 2 + partials
     bad = twell.make_shape(16, 2048, 8192, 100, 4, __import__("torch").bfloat16)
     assert twell.ffn_workspace_bytes(bad) == 0
 

@@ -168,6 +168,11 @@ SMALL = [
     ("hybrid_stress_bf16", 520, 512, 1536),
     ("large_bf16", 257, 192, 1280),
     ("decode_bf16", 16, 256, 512),
+    # at most 64 rows: split-K partial sums (MFMA when d_model is a multiple of
+    # 64, the general up-projection kernel otherwise), 33..64 rows on 64-row blocks
+    ("decode_bf16", 16, 136, 1024),
+    ("ffn_1b_bf16", 64, 576, 1280),
+    ("decode_bf16", 3, 4096, 2048),
     # d_model/8 a whole 4, 8 or 16 bf16 per lane: the XCD-sliced sparse product
     ("ffn_1b_bf16", 150, 2048, 512),
     ("hybrid_stress_bf16", 40, 4096, 384),
