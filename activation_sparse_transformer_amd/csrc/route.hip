@@ -1,8 +1,9 @@
 // Row routing and the dense <-> TwELL conversions.
 //
-//  G2a route_scan   per-row OR of the tile-overflow flags, ascending numbering
-//                   of the dense rows (one workgroup, block-wide prefix scan,
-//                   so the order is deterministic);
+//  G2a route_scan   per-row OR of the tile-overflow flags (row_or for more
+//                   than 1024 rows), ascending numbering of the dense rows
+//                   (one workgroup, block-wide prefix scan, so the order is
+//                   deterministic);
 //  G2b materialize  dense_values[m] = full row of h for each dense row, then
 //                   the row's TwELL slots are cleared;
 //  G5  pack_tiles   dense_to_twell of an existing h, one wave per (row, tile);
@@ -63,17 +64,30 @@ __global__ __launch_bounds__(kRowThreads) void row_or_kernel(const uint8_t* __re
   if (n < N) row_dense[n] = row_has_flag(flags + n * nt, nt) ? 1 : 0;
 }
 
+// One workgroup: thread i takes a run of consecutive rows (with `flags`, it
+// first ORs each row's tile flags into row_dense; otherwise row_dense is
+// given), then a block-wide prefix scan of the per-thread dense counts
+// numbers the dense rows in ascending order.
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(
-    const uint8_t* __restrict__ row_dense, int64_t N, int32_t* __restrict__ row_map,
-    int32_t* __restrict__ dense_rows, int64_t cap, int32_t* __restrict__ n_dense,
-    int32_t* __restrict__ sparse_rows, int32_t* __restrict__ n_sparse,
-    int32_t* __restrict__ status) {
+    const uint8_t* __restrict__ flags, int nt, uint8_t* __restrict__ row_dense, int64_t N,
+    int32_t* __restrict__ row_map, int32_t* __restrict__ dense_rows, int64_t cap,
+    int32_t* __restrict__ n_dense, int32_t* __restrict__ sparse_rows,
+    int32_t* __restrict__ n_sparse, int32_t* __restrict__ status) {
   __shared__ int wave_tot[kScanThreads / kWave];
   const int tid = threadIdx.x;
   const int64_t per = (N + kScanThreads - 1) / kScanThreads;
   const int64_t r0 = min(N, tid * per), r1 = min(N, r0 + per);
   int local = 0;
-  for (int64_t n = r0; n < r1; ++n) local += row_dense[n];
+  for (int64_t n = r0; n < r1; ++n) {
+    uint8_t d;
+    if (flags != nullptr) {
+      d = row_has_flag(flags + n * nt, nt) ? 1 : 0;
+      row_dense[n] = d;
+    } else {
+      d = row_dense[n];
+    }
+    local += d;
+  }
   const int incl = wave_inclusive_scan(local);
   const int wave = tid / kWave, lane = lane_id();
   if (lane == kWave - 1) wave_tot[wave] = incl;
@@ -268,13 +282,16 @@ __global__ __launch_bounds__(kRowThreads) void unpack_kernel(
 
 hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* dense_rows,
                              int64_t dense_cap, int32_t* n_dense, int32_t* status, hipStream_t s) {
-  if (g.n_rows > 0) {
+  // Up to one row per scan thread the scan ORs the flags itself; beyond
+  // that a row-parallel pass does it first.
+  const bool fused = g.n_rows <= kScanThreads;
+  if (!fused) {
     const unsigned blocks = static_cast<unsigned>((g.n_rows + kRowThreads - 1) / kRowThreads);
     row_or_kernel<<<blocks, kRowThreads, 0, s>>>(rb.flags, g.n_rows, g.n_tiles, rb.row_dense);
   }
-  route_scan_kernel<<<1, kScanThreads, 0, s>>>(rb.row_dense, g.n_rows, rb.row_map, dense_rows,
-                                               dense_cap, n_dense, rb.sparse_rows, rb.n_sparse,
-                                               status);
+  route_scan_kernel<<<1, kScanThreads, 0, s>>>(fused ? rb.flags : nullptr, g.n_tiles, rb.row_dense, g.n_rows,
+                                               rb.row_map, dense_rows, dense_cap, n_dense,
+                                               rb.sparse_rows, rb.n_sparse, status);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kSkThreads = 256;
 constexpr int kSkKC = 256;      // K per LDS chunk of A, up-projection
-constexpr int kSkKCDown = 128;  // K per LDS chunk of A, fallback
+constexpr int kSkKCDown = 64;   // K per LDS chunk of A, fallback
 constexpr int kSkLoads = 16;    // weight loads a thread keeps in flight
 constexpr int kSkSumBatch = 8;  // partial-sum loads in flight per output
 
@@ -60,51 +60,56 @@ struct Raw {
   }
 };
 
-// Rows [0, M) of A[:, k0 .. k0 + KC) into LDS as float [MM][KC]; rows >= M
-// and columns >= K are zero.
-template <typename E, int MM, int KC>
-__device__ __forceinline__ void stage_a(float* sA, const E* __restrict__ A, int64_t lda, int M,
-                                        int k0, int K) {
-  for (int e = threadIdx.x; e < MM * KC; e += kSkThreads) {
+// Rows per workgroup of the fp32 partial kernels: blockIdx.z picks the group
+// of kSkRows rows [z * kSkRows, ...) of A.
+constexpr int kSkRows = 16;
+
+// Rows [r0, r0 + kSkRows) ∩ [0, M) of A[:, k0 .. k0 + KC) into LDS as float
+// [kSkRows][KC]; other rows and columns >= K are zero.
+template <typename E, int KC>
+__device__ __forceinline__ void stage_a(float* sA, const E* __restrict__ A, int64_t lda, int r0,
+                                        int M, int k0, int K) {
+  for (int e = threadIdx.x; e < kSkRows * KC; e += kSkThreads) {
     const int m = e / KC, k = e - m * KC;
     float v = 0.f;
-    if (m < M && k0 + k < K) v = ElemTraits<E>::to_f32(A[static_cast<int64_t>(m) * lda + k0 + k]);
+    if (r0 + m < M && k0 + k < K)
+      v = ElemTraits<E>::to_f32(A[static_cast<int64_t>(r0 + m) * lda + k0 + k]);
     sA[e] = v;
   }
 }
 
-// Columns per thread of skinny_kn_partial: 16, 8 or 4 bytes of E per weight
-// row, so the MM x CPT accumulators and kSkLoads rows of loads fit in VGPRs.
-template <typename E, int MM>
+// Columns per thread of skinny_kn_partial: 16 bytes of E per weight row.
+template <typename E>
 constexpr int kn_cols() {
-  return (MM <= 16 ? 16 : MM <= 32 ? 8 : 4) / static_cast<int>(sizeof(E));
+  return 16 / static_cast<int>(sizeof(E));
 }
 
 // Weight [K][N] (N-contiguous): thread t owns CPT consecutive columns and
 // walks the slice's K range kSkLoads rows at a time, all of a batch's loads
 // issued before any is used; the A rows are restaged in LDS every KC.
-template <typename E, int MM>
+template <typename E>
 __global__ __launch_bounds__(kSkThreads) void skinny_kn_partial(
     const E* __restrict__ A, int64_t lda, const int32_t* __restrict__ m_dev, int m_cap, int K,
-    int N, int kw, const E* __restrict__ W, float* __restrict__ part) {
-  constexpr int CPT = kn_cols<E, MM>();
+    int N, int kw, int mm, const E* __restrict__ W, float* __restrict__ part) {
+  constexpr int CPT = kn_cols<E>();
   constexpr int KC = kSkKCDown, U = kSkLoads;
   static_assert(KC % U == 0, "whole load batches per chunk");
-  __shared__ __attribute__((aligned(16))) float sA[MM * KC];
+  __shared__ __attribute__((aligned(16))) float sA[kSkRows * KC];
   const int M = m_dev != nullptr ? min(*m_dev, m_cap) : m_cap;
-  if (M <= 0) return;
+  const int r0 = blockIdx.z * kSkRows;
+  if (r0 >= M) return;
   const int slice = blockIdx.y, kbeg = slice * kw, kfin = min(kbeg + kw, K);
   const int n = (blockIdx.x * kSkThreads + threadIdx.x) * CPT;
   const bool live = n < N;  // N is a multiple of 8: a thread's columns are all in or all out
   const int nc = live ? n : 0;
-  float acc[MM][CPT];
+  float acc[kSkRows][CPT];
 #pragma unroll
-  for (int m = 0; m < MM; ++m)
+  for (int m = 0; m < kSkRows; ++m)
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[m][c] = 0.f;
   for (int k0 = kbeg; k0 < kfin; k0 += KC) {
     __syncthreads();  // the previous chunk's A is no longer read
-    stage_a<E, MM, KC>(sA, A, lda, M, k0, K);
+    stage_a<E, KC>(sA, A, lda, r0, M, k0, K);
     __syncthreads();
     const int kend = min(KC, kfin - k0);
     for (int k = 0; k < kend; k += U) {
@@ -116,7 +121,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kn_partial(
         w[j].load(W + static_cast<int64_t>(k0 + kr) * N + nc);
       }
 #pragma unroll
-      for (int m = 0; m < MM; ++m) {
+      for (int m = 0; m < kSkRows; ++m) {
 #pragma unroll
         for (int j4 = 0; j4 < U; j4 += 4) {
           const float4 a = *reinterpret_cast<const float4*>(sA + m * KC + k + j4);
@@ -130,33 +135,34 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kn_partial(
     }
   }
   if (!live) return;
-  float* dst = part + static_cast<int64_t>(slice) * MM * N + n;
+  float* dst = part + (static_cast<int64_t>(slice) * mm + r0) * N + n;
 #pragma unroll
-  for (int m = 0; m < MM; ++m)
-    if (m < M)
+  for (int m = 0; m < kSkRows; ++m)
+    if (r0 + m < M)
 #pragma unroll
       for (int c = 0; c < CPT; ++c) dst[static_cast<int64_t>(m) * N + c] = acc[m][c];
 }
 
 // Weight [N][K] (K-contiguous): thread t owns column n = one weight row and
 // reads the slice's K range 16 bytes at a time, kSkLoads / 2 loads in flight.
-template <typename E, int MM>
+template <typename E>
 __global__ __launch_bounds__(kSkThreads) void skinny_nk_partial(
-    const E* __restrict__ A, int64_t lda, int M, int K, int N, int kw, const E* __restrict__ W,
-    float* __restrict__ part) {
+    const E* __restrict__ A, int64_t lda, int M, int K, int N, int kw, int mm,
+    const E* __restrict__ W, float* __restrict__ part) {
   constexpr int V = Vec16B<E>::N, KC = kSkKC, U = kSkLoads / 2;
   static_assert(KC % (V * U) == 0, "whole load batches per chunk");
-  __shared__ __attribute__((aligned(16))) float sA[MM * KC];
+  __shared__ __attribute__((aligned(16))) float sA[kSkRows * KC];
+  const int r0 = blockIdx.z * kSkRows;
   const int slice = blockIdx.y, kbeg = slice * kw, kfin = min(kbeg + kw, K);
   const int n = blockIdx.x * kSkThreads + threadIdx.x;
   const bool live = n < N;
-  float acc[MM];
+  float acc[kSkRows];
 #pragma unroll
-  for (int m = 0; m < MM; ++m) acc[m] = 0.f;
+  for (int m = 0; m < kSkRows; ++m) acc[m] = 0.f;
   const E* wrow = W + static_cast<int64_t>(live ? n : 0) * K;
   for (int k0 = kbeg; k0 < kfin; k0 += KC) {
     __syncthreads();
-    stage_a<E, MM, KC>(sA, A, lda, M, k0, K);
+    stage_a<E, KC>(sA, A, lda, r0, M, k0, K);
     __syncthreads();
     const int kend = min(KC, kfin - k0);  // a multiple of V: K is
     for (int k = 0; k < kend; k += V * U) {
@@ -171,7 +177,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_nk_partial(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int m = 0; m < MM; ++m) {
+        for (int m = 0; m < kSkRows; ++m) {
 #pragma unroll
           for (int q = 0; q < V; q += 4) {
             const float4 a = *reinterpret_cast<const float4*>(sA + m * KC + k + u * V + q);
@@ -185,10 +191,10 @@ __global__ __launch_bounds__(kSkThreads) void skinny_nk_partial(
     }
   }
   if (!live) return;
-  float* dst = part + static_cast<int64_t>(slice) * MM * N + n;
+  float* dst = part + (static_cast<int64_t>(slice) * mm + r0) * N + n;
 #pragma unroll
-  for (int m = 0; m < MM; ++m)
-    if (m < M) dst[static_cast<int64_t>(m) * N] = acc[m];
+  for (int m = 0; m < kSkRows; ++m)
+    if (r0 + m < M) dst[static_cast<int64_t>(m) * N] = acc[m];
 }
 
 // Sum over slices of part[slice][m][n] (slice stride `stride`), in slice
@@ -223,60 +229,94 @@ __global__ __launch_bounds__(kSkThreads) void skinny_fallback_reduce(
   if (r >= 0 && r < y_rows) y[r * N + n] = ElemTraits<E>::from_f32(s);
 }
 
-// Up-projection epilogue, one workgroup per tile t: h[m][t*T + c] =
-// ReLU(sum over slices + b) rounded, staged in LDS, then each wave packs rows
-// m = wave, wave + 4, ... of the tile.
+// Up-projection epilogue, one workgroup per (tile t, group of 4 rows):
+// h[m][t*T + c] = ReLU(sum over slices + b) rounded, staged in LDS, then wave
+// w packs row 4 blockIdx.y + w of the tile.
+constexpr int kPackRows = kSkThreads / kWave;
+
 template <typename E>
 __global__ __launch_bounds__(kSkThreads) void skinny_up_pack(
     const float* __restrict__ part, int ks, int mm, int M, int dff, int T, int C, int nt,
     const float* __restrict__ bias, E* __restrict__ vals, uint8_t* __restrict__ idx,
     uint8_t* __restrict__ cnt, uint8_t* __restrict__ flags, E* __restrict__ spill,
     E* __restrict__ hdebug) {
-  __shared__ __attribute__((aligned(16))) E sh[kSkinnyMaxRows * 256];
-  const int t = blockIdx.x;
+  constexpr int EPT = kPackRows * 256 / kSkThreads;  // elements per thread, T <= 256
+  __shared__ __attribute__((aligned(16))) E sh[kPackRows * 256];
+  const int t = blockIdx.x, r0 = blockIdx.y * kPackRows;
+  const int rows = min(kPackRows, M - r0);
   const int c0 = t * T;
-  for (int e = threadIdx.x; e < M * T; e += kSkThreads) {
+  const int64_t stride = static_cast<int64_t>(mm) * dff;
+  // all slice loads of all of this thread's elements in flight together
+  float z[EPT];
+  int64_t off[EPT];
+  bool ok[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + j * kSkThreads;
     const int m = e / T, c = e - m * T;
-    const float z = slice_sum(part + static_cast<int64_t>(m) * dff + c0 + c, ks,
-                              static_cast<int64_t>(mm) * dff) + bias[c0 + c];
-    const E h = ElemTraits<E>::from_f32(z > 0.f ? z : 0.f);
+    ok[j] = m < rows;
+    off[j] = static_cast<int64_t>(ok[j] ? r0 + m : r0) * dff + c0 + (ok[j] ? c : 0);
+    z[j] = 0.f;
+  }
+  for (int kc = 0; kc < ks; kc += kSkSumBatch) {
+    float v[EPT][kSkSumBatch];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+#pragma unroll
+      for (int u = 0; u < kSkSumBatch; ++u) {
+        const int q = kc + u < ks ? kc + u : kc;  // past the end: reread, then drop
+        v[j][u] = part[q * stride + off[j]];
+      }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+#pragma unroll
+      for (int u = 0; u < kSkSumBatch; ++u)
+        if (kc + u < ks) z[j] += v[j][u];
+  }
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = threadIdx.x + j * kSkThreads;
+    if (!ok[j]) continue;
+    const int m = e / T, c = e - m * T;
+    const float zz = z[j] + bias[c0 + c];
+    const E h = ElemTraits<E>::from_f32(zz > 0.f ? zz : 0.f);
     sh[m * T + c] = h;
-    if (hdebug != nullptr) hdebug[static_cast<int64_t>(m) * dff + c0 + c] = h;
+    if (hdebug != nullptr) hdebug[static_cast<int64_t>(r0 + m) * dff + c0 + c] = h;
   }
   __syncthreads();
   const int wave = threadIdx.x / kWave;
-  for (int m = wave; m < M; m += kSkThreads / kWave) {
+  if (wave < rows) {
+    const int m = r0 + wave;
     const int64_t q = static_cast<int64_t>(m) * nt + t;
-    pack_tile_from<E>(sh + m * T, T, C, vals + q * C, idx + q * C, cnt + q, flags + q,
+    pack_tile_from<E>(sh + wave * T, T, C, vals + q * C, idx + q * C, cnt + q, flags + q,
                       spill != nullptr ? spill + static_cast<int64_t>(m) * dff + c0 : nullptr);
   }
 }
 
 int rows_bucket(int64_t m) { return m <= 16 ? 16 : m <= 32 ? 32 : 64; }
 
-template <int MM>
-hipError_t up_f32_mm(const Geometry& g, const float* x, const float* w_up_t, const float* b_up,
-                     const PackOut& out, float* part, hipStream_t s) {
+hipError_t up_f32(const Geometry& g, const float* x, const float* w_up_t, const float* b_up,
+                  const PackOut& out, float* part, hipStream_t s) {
   const int M = static_cast<int>(g.n_rows), N = g.d_ff, K = g.d_model;
-  const int nb = (N + kSkThreads - 1) / kSkThreads;
-  const SkinnySplit sp = skinny_split(g.n_rows, K, nb, kSkKC, 512);
-  skinny_nk_partial<float, MM><<<dim3(nb, sp.slices), kSkThreads, 0, s>>>(x, K, M, K, N, sp.kw,
-                                                                          w_up_t, part);
+  const int nb = (N + kSkThreads - 1) / kSkThreads, nz = (M + kSkRows - 1) / kSkRows;
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkKC, 512);
+  skinny_nk_partial<float><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(x, K, M, K, N, sp.kw,
+                                                                          sp.mm, w_up_t, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_skinny_up_epilogue<float>(g, sp, part, b_up, out, s);
 }
 
-template <int MM>
-hipError_t fallback_f32_mm(const Geometry& g, const float* a, const int32_t* dense_rows,
-                           const int32_t* n_dense, int m_cap, const float* w_down, float* y,
-                           float* part, hipStream_t s) {
-  constexpr int CPT = kn_cols<float, MM>();
+hipError_t fallback_f32(const Geometry& g, const float* a, const int32_t* dense_rows,
+                        const int32_t* n_dense, int m_cap, const float* w_down, float* y,
+                        float* part, hipStream_t s) {
+  constexpr int CPT = kn_cols<float>();
   const int N = g.d_model, K = g.d_ff;
   const int nb = (N + kSkThreads * CPT - 1) / (kSkThreads * CPT);
-  const SkinnySplit sp = skinny_split(g.n_rows, K, nb, kSkKCDown, 512);
-  skinny_kn_partial<float, MM><<<dim3(nb, sp.slices), kSkThreads, 0, s>>>(
-      a, K, n_dense, m_cap, K, N, sp.kw, w_down, part);
+  const int nz = (m_cap + kSkRows - 1) / kSkRows;
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkKCDown, 512);
+  skinny_kn_partial<float><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(
+      a, K, n_dense, m_cap, K, N, sp.kw, sp.mm, w_down, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_skinny_fallback_reduce<float>(g, sp, part, n_dense, m_cap, dense_rows, y, s);
@@ -303,7 +343,8 @@ template <typename E>
 hipError_t launch_skinny_up_epilogue(const Geometry& g, const SkinnySplit& sp, const float* part,
                                      const float* b_up, const PackOut& out, hipStream_t s) {
   if (g.tile > 256) return hipErrorInvalidValue;  // the tile is staged in LDS
-  skinny_up_pack<E><<<g.n_tiles, kSkThreads, 0, s>>>(
+  const unsigned groups = static_cast<unsigned>((g.n_rows + kPackRows - 1) / kPackRows);
+  skinny_up_pack<E><<<dim3(g.n_tiles, groups), kSkThreads, 0, s>>>(
       part, sp.slices, sp.mm, static_cast<int>(g.n_rows), g.d_ff, g.tile, g.capacity, g.n_tiles,
       b_up, static_cast<E*>(out.vals), out.idx, out.cnt, out.flags, static_cast<E*>(out.spill),
       static_cast<E*>(out.h_debug));
@@ -324,11 +365,7 @@ hipError_t launch_skinny_fallback_reduce(const Geometry& g, const SkinnySplit& s
 hipError_t launch_skinny_up_pack_f32(const Geometry& g, const float* x, const float* w_up_t,
                                      const float* b_up, const PackOut& out, float* part,
                                      hipStream_t s) {
-  switch (rows_bucket(g.n_rows)) {
-    case 16: return up_f32_mm<16>(g, x, w_up_t, b_up, out, part, s);
-    case 32: return up_f32_mm<32>(g, x, w_up_t, b_up, out, part, s);
-    default: return up_f32_mm<64>(g, x, w_up_t, b_up, out, part, s);
-  }
+  return up_f32(g, x, w_up_t, b_up, out, part, s);
 }
 
 hipError_t launch_skinny_fallback_f32(const Geometry& g, const float* a, const int32_t* dense_rows,
@@ -336,12 +373,7 @@ hipError_t launch_skinny_fallback_f32(const Geometry& g, const float* a, const i
                                       const float* w_down, float* y, float* part, hipStream_t s) {
   const int64_t worst = dense_cap < g.n_rows ? dense_cap : g.n_rows;
   if (worst <= 0) return hipSuccess;
-  const int m_cap = static_cast<int>(worst);
-  switch (rows_bucket(g.n_rows)) {
-    case 16: return fallback_f32_mm<16>(g, a, dense_rows, n_dense, m_cap, w_down, y, part, s);
-    case 32: return fallback_f32_mm<32>(g, a, dense_rows, n_dense, m_cap, w_down, y, part, s);
-    default: return fallback_f32_mm<64>(g, a, dense_rows, n_dense, m_cap, w_down, y, part, s);
-  }
+  return fallback_f32(g, a, dense_rows, n_dense, static_cast<int>(worst), w_down, y, part, s);
 }
 
 template hipError_t launch_skinny_up_epilogue<uint16_t>(const Geometry&, const SkinnySplit&,

@@ -275,6 +275,84 @@ __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
   }
 }
 
+// Few rows (decode-sized batches): one workgroup of P waves per (row, XCD
+// column slice), wave w taking tiles [w * tpw, (w + 1) * tpw) of the row, so
+// the row's gathers run P ways in parallel instead of one after the other.
+// The P partial sums meet in LDS and are added in wave order.
+template <int VEC, int P>
+__global__ __launch_bounds__(P * kWave) void spmm_split_bf16_kernel(
+    const uint16_t* __restrict__ vals, const uint8_t* __restrict__ idx,
+    const uint8_t* __restrict__ cnt, const int32_t* __restrict__ rows,
+    const int32_t* __restrict__ n_rows_dev, const uint16_t* __restrict__ w,
+    uint16_t* __restrict__ y, int64_t N, int dm, int T, int C, int nt, int n_slices, int tpw) {
+  extern __shared__ uint2 spmm_lists[];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wslots = tpw * C;
+  uint2* list = spmm_lists + wave * wslots;
+  float* red = reinterpret_cast<float*>(spmm_lists + P * wslots);  // [P][VEC][64]
+  const int xcd = blockIdx.x % 8;
+  const int slice = xcd % n_slices;
+  const int parts = 8 / n_slices;
+  const int part = xcd / n_slices;
+  const int64_t per_xcd = gridDim.x / 8;
+  const int col = slice * (kWave * VEC) + lane * VEC;
+  const char* wbase = reinterpret_cast<const char*>(w + col);
+  const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
+  const int t0 = wave * tpw, t1 = min(nt, t0 + tpw);
+  for (int64_t k = part + parts * static_cast<int64_t>(blockIdx.x / 8); k < R;
+       k += parts * per_xcd) {
+    const int64_t n = rows != nullptr ? rows[k] : k;
+    const int64_t s0 = n * nt * C;
+    int nnz = 0;
+    for (int g = t0 * C; g < t1 * C; g += kWave) {
+      const int s = g + lane;
+      bool live = false;
+      uint32_t off = 0, v = 0;
+      if (s < t1 * C) {
+        const int t = s / C;
+        const int kk = s - t * C;
+        if (kk < static_cast<int>(cnt[n * nt + t])) {
+          const int local = static_cast<int>(idx[s0 + s]);
+          live = local < T;  // a malformed index is ignored rather than read out of bounds
+          off = static_cast<uint32_t>(t * T + local) * static_cast<uint32_t>(dm) * 2u;
+          v = vals[s0 + s];
+        }
+      }
+      const uint64_t m = wave_ballot(live);
+      if (live) list[nnz + popc_below(m)] = make_uint2(off, v);
+      nnz += popc64(m);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's list is in LDS
+    float acc[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+    for (int q = 0; q < nnz; q += kListUnroll) {
+      uint2 e[kListUnroll];
+      WVec<VEC> wv[kListUnroll];
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u) {
+        e[u] = list[min(q + u, nnz - 1)];  // past the end: reread the last entry, unused
+        load_wvec<VEC>(wv[u], reinterpret_cast<const uint16_t*>(wbase + e[u].x));
+      }
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u)
+        if (q + u < nnz) dot2_row<VEC>(acc, e[u].y, e[u].y << 16, wv[u]);
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) red[(wave * VEC + i) * kWave + lane] = acc[i];
+    __syncthreads();
+    // wave w finishes columns i = w, w + P, ... of each lane's VEC
+    uint16_t* dst = y + n * dm + col;
+    for (int i = wave; i < VEC; i += P) {
+      float sum = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) sum += red[(p * VEC + i) * kWave + lane];
+      dst[i] = ElemTraits<uint16_t>::from_f32(sum);
+    }
+    __syncthreads();  // red and the lists are reused by the next row
+  }
+}
+
 }  // namespace
 
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
@@ -305,6 +383,27 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
       const uint16_t* v16 = static_cast<const uint16_t*>(vals);
       const uint16_t* w16 = static_cast<const uint16_t*>(w_down);
       uint16_t* y16 = static_cast<uint16_t*>(y);
+      // Few rows: split each row over the 16 waves of a workgroup.
+      constexpr int P = 16;
+      const int tpw = (g.n_tiles + P - 1) / P;
+      const size_t split_bytes = static_cast<size_t>(P) * tpw * g.capacity * 8 +
+                                 static_cast<size_t>(P) * vec * kWave * 4;
+      if (g.n_rows * n_slices <= 1024 && split_bytes <= 64 * 1024) {
+        const int64_t rows_per_xcd = (g.n_rows + (8 / n_slices) - 1) / (8 / n_slices);
+        const unsigned sblocks = static_cast<unsigned>(8 * rows_per_xcd);
+        const uint16_t* v16 = static_cast<const uint16_t*>(vals);
+        const uint16_t* w16 = static_cast<const uint16_t*>(w_down);
+        uint16_t* y16 = static_cast<uint16_t*>(y);
+        if (vec == 8)
+          spmm_split_bf16_kernel<8, P><<<sblocks, P * kWave, split_bytes, s>>>(
+              v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity,
+              g.n_tiles, n_slices, tpw);
+        else
+          spmm_split_bf16_kernel<16, P><<<sblocks, P * kWave, split_bytes, s>>>(
+              v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity,
+              g.n_tiles, n_slices, tpw);
+        return hipGetLastError();
+      }
       if (vec == 8)
         spmm_list_bf16_kernel<8><<<xblocks, kThreads, list_bytes, s>>>(
             v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
