@@ -179,6 +179,9 @@ SMALL = [
     ("large_bf16", 24, 8192, 512),
     # a float32 row longer than 64 KB: dense rows rebuilt without the LDS row buffer
     ("tiny_fp32", 20, 64, 16448),
+    # bf16 rows over 20 KB with 4 or 8 slots per tile: dense rows rebuilt from slot groups
+    ("ffn_1b_bf16", 70, 128, 10368),
+    ("large_bf16", 33, 64, 10752),
 ]
 
 
