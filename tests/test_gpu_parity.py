@@ -49,6 +49,20 @@ def test_pack_unpack_bitexact(dtype, T, C, density, n):
     np.testing.assert_array_equal(u32(as_f32(u)), u32(oracle.unpack(ref)))
 
 
+@pytest.mark.parametrize("n,dff,T,density", [(1024, 1024, 64, 0.02), (1000, 192, 64, 0.06),
+                                             (1025, 1024, 64, 0.02), (2500, 200 * 64, 64, 0.01)])
+def test_pack_routing_row_counts(n, dff, T, density):
+    """Row routing with the row flags ORed inside the scan (up to 1024 rows)
+    and by the separate row pass beyond, tile counts a multiple of 16 or not."""
+    say(f"pack routing n={n} dff={dff} T={T}")
+    ht, hh = sparse_h(77 + n, n, dff, density, torch.bfloat16)
+    hy, status = twell.twell_pack(ht.cuda(), T, 4)
+    torch.cuda.synchronize()
+    assert int(status.item()) == twell.TWELL_OK
+    ref = assert_pack_matches(hy, hh)
+    assert 0 < ref.n_dense < n
+
+
 def test_pack_all_zero_and_all_dense():
     for fill, dense in ((0.0, False), (1.5, True)):
         h = torch.full((40, 512), fill, dtype=torch.bfloat16, device="cuda")
