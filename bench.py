@@ -5,9 +5,10 @@
 One step = one full ffn_sparse_forward (up-projection + fused TwELL pack,
 row routing, sparse down-projection, dense fallback) over one batch of
 seeded synthetic tokens already resident in HBM.  Between steps a 1 GiB
-buffer is rewritten so the 256 MB Infinity Cache no longer holds the weights
+buffer is read so the 256 MB Infinity Cache no longer holds the weights
 (cold cache: in a real model other layers run between two calls of one FFN
-layer).  Each stage is timed with HIP events recorded by the library on the
+layer); reading rather than writing it leaves clean lines, so the timed
+kernels pay no write-backs of the eviction's data.  Each stage is timed with HIP events recorded by the library on the
 stream its kernels run on.
 
 Prints ONE JSON line.  Besides the throughput it carries the roofline of the
@@ -191,8 +192,11 @@ def hybrid_stats(cfg, bufs):
     return n_dense, nnz_sparse, n_unique
 
 
-def cpu_oracle_baseline(t, cfg, target_s=10.0):
-    """The CPU oracle (float64 dense FFN) on a bounded, seeded sample of rows."""
+def cpu_oracle_baseline(t, cfg, target_s=15.0):
+    """The CPU oracle (float64 dense FFN) on a bounded, seeded sample of rows.
+
+    The per-row cost is calibrated on 256 rows; whole passes run faster per
+    row than that, so a 15 s target lands at about 10 s of work."""
     import oracle  # test infrastructure: only this leg of the benchmark uses it
 
     try:
@@ -330,7 +334,7 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "cache": "cold (1 GiB rewritten between steps)",
+        "cache": "cold (1 GiB read between steps)",
         "config": {
             "workload": cfg.name, "n_rows": N, "d_model": dm, "d_ff": dff, "tile": cfg.tile,
             "capacity": C, "b0": cfg.b0, "seed": cfg.seed,
