@@ -1,6 +1,6 @@
 """Benchmark of the hybrid-TwELL ReLU FFN forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--capacity C]
 
 One step = one full ffn_sparse_forward (up-projection + fused TwELL pack,
 row routing, sparse down-projection, dense fallback) over one batch of
@@ -237,6 +237,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ffn_1b_bf16", choices=sorted(CONFIGS))
+    ap.add_argument("--capacity", type=int, default=None,
+                    help="slots per tile instead of the workload's own (same inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-baseline", action="store_true")
     args = ap.parse_args(argv)
@@ -248,6 +250,8 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     cfg = CONFIGS[args.workload]
+    if args.capacity is not None:
+        cfg = cfg.replace(capacity=args.capacity)
     dev = torch.device("cuda:0")
     log(f"[bench] workload {cfg.name}: generating inputs")
     t = make_inputs(cfg)
