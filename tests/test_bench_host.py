@@ -1,0 +1,39 @@
+"""Host-side logic of bench.py (no GPU): argument handling and the reading of
+the committed hardware-counter summary."""
+import os
+
+import bench
+
+
+def test_more_than_one_gpu_exits_with_a_message(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
+
+
+def test_recorded_traffic_sums_kernels_and_drops_stale_stages(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "w_hbm_traffic.txt").write_text(
+        "# comment\n"
+        "fetch_scale 2.0\n"
+        "stage route kernel row_or_kernel src_sha good fetch_kib 1 write_kib 1 bytes 100\n"
+        "stage route kernel materialize_kernel src_sha good fetch_kib 1 write_kib 1 bytes 250\n"
+        "stage spmm_sparse kernel spmm_list_bf16_kernel src_sha stale fetch_kib 1 write_kib 1 bytes 7\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_sha", lambda stage: "good")
+    t = bench.recorded_traffic("w")
+    assert t["route"] == 350.0
+    assert t["spmm_sparse"] is None  # sources changed since the counters were taken
+    assert t["up_gemm_pack"] is None and t["fallback_gemm"] is None  # not recorded
+
+
+def test_recorded_traffic_without_a_summary(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert all(v is None for v in bench.recorded_traffic("nothing").values())
+
+
+def test_stage_sources_exist():
+    for stage, files in bench.STAGE_SOURCES.items():
+        for f in files:
+            assert os.path.exists(os.path.join(bench.ROOT, f)), (stage, f)
+        assert len(bench.source_sha(stage)) == 16
