@@ -243,15 +243,22 @@ def test_forward_bias_limits(dtype):
     assert_close_rel(as_f64(out.y), y_ref, TOL[cfg.torch_dtype])
 
 
-def test_forward_dense_capacity_exceeded():
-    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=200, d_model=128, d_ff=1024)
+@pytest.mark.parametrize("n_rows", [200, 1500])
+def test_forward_dense_capacity_exceeded(n_rows):
+    """Too many dense rows: the status says so, n_dense is the true count and
+    the first dense_capacity dense rows are stored, whether the capacity runs
+    out early or at the last dense row, with the row flags ORed inside the
+    scan (200 rows) or by the separate row pass (1500 rows)."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=128, d_ff=1024)
     t = make_inputs(cfg)
-    out = run_forward(cfg, t, dense_capacity=3)
-    h_ref = oracle.pack(as_f32(out.h_debug), cfg.tile, cfg.capacity)
-    assert h_ref.n_dense > 3
-    assert int(out.status.item()) == twell.TWELL_ERR_DENSE_CAPACITY
-    assert out.hybrid.n_dense_host() == h_ref.n_dense
-    np.testing.assert_array_equal(out.hybrid.dense_rows.cpu().numpy(), h_ref.dense_rows[:3])
+    total = run_forward(cfg, t).hybrid.n_dense_host()
+    for cap in (3, total - 1):
+        out = run_forward(cfg, t, dense_capacity=cap)
+        h_ref = oracle.pack(as_f32(out.h_debug), cfg.tile, cfg.capacity)
+        assert h_ref.n_dense == total > cap
+        assert int(out.status.item()) == twell.TWELL_ERR_DENSE_CAPACITY
+        assert out.hybrid.n_dense_host() == total
+        np.testing.assert_array_equal(out.hybrid.dense_rows.cpu().numpy(), h_ref.dense_rows[:cap])
 
 
 def test_forward_zero_rows():
