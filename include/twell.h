@@ -124,13 +124,17 @@ int twell_version(void);
 const char* twell_status_string(int status);
 
 /* Bytes of device workspace ffn_sparse_forward needs for this shape
- * (0 for an invalid shape).  Sized for the worst case: every tile spilled. */
+ * (0 for an invalid shape).  Sized for the worst case: every tile spilled;
+ * batches of at most 64 rows add room for fp32 split-K partial sums. */
 size_t ffn_sparse_workspace_size(const twell_shape* shape);
 
 /* The fused forward pass: y = ReLU(x W_up + b_up) W_down, with the hidden
  * activations h produced directly in hybrid TwELL form.
  *   1. up-projection GEMM (MFMA for bf16) + bias + ReLU + rounding, whose
- *      epilogue packs each (row, tile) of h into TwELL and flags overflow;
+ *      epilogue packs each (row, tile) of h into TwELL and flags overflow
+ *      (at most 64 rows: K is split over workgroups whose fp32 partial sums
+ *      are added in a fixed order before the same epilogue; likewise for
+ *      the fallback of step 4);
  *   2. row routing: a row with an overflowing tile is dense; dense rows are
  *      numbered in ascending order and copied to dense_values, their TwELL
  *      slots cleared;
@@ -143,7 +147,7 @@ size_t ffn_sparse_workspace_size(const twell_shape* shape);
  * call, kept until the process ends), forked from and joined back into
  * `stream` with events, so all work still completes in `stream` order and the
  * pass can be captured into a HIP graph from `stream`.  Calls on one device
- * share that auxiliary stream. 
+ * share that auxiliary stream.
  * Arguments: shape (host pointer); x, w_up_t, b_up, w_down inputs; y output;
  * h_out (host pointer to a struct of device pointers) receives h in hybrid
  * TwELL form; h_dense_debug, if non-NULL, receives h [n_rows][d_ff] exactly
