@@ -60,16 +60,19 @@ struct Raw {
   }
 };
 
-// Rows per workgroup of the fp32 partial kernels: blockIdx.z picks the group
-// of kSkRows rows [z * kSkRows, ...) of A.
+// Rows per workgroup of the fp32 partial kernels (R): blockIdx.z picks the
+// group of R rows [z * R, ...) of A.  16 as a rule; 4 when the grid would
+// otherwise have too few workgroups to spread over the CUs (tiny layers).
 constexpr int kSkRows = 16;
+constexpr int kSkRowsSmall = 4;
+constexpr int kSkMinBlocks = 64;
 
-// Rows [r0, r0 + kSkRows) ∩ [0, M) of A[:, k0 .. k0 + KC) into LDS as float
-// [kSkRows][KC]; other rows and columns >= K are zero.
-template <typename E, int KC>
+// Rows [r0, r0 + R) ∩ [0, M) of A[:, k0 .. k0 + KC) into LDS as float
+// [R][KC]; other rows and columns >= K are zero.
+template <typename E, int KC, int R>
 __device__ __forceinline__ void stage_a(float* sA, const E* __restrict__ A, int64_t lda, int r0,
                                         int M, int k0, int K) {
-  for (int e = threadIdx.x; e < kSkRows * KC; e += kSkThreads) {
+  for (int e = threadIdx.x; e < R * KC; e += kSkThreads) {
     const int m = e / KC, k = e - m * KC;
     float v = 0.f;
     if (r0 + m < M && k0 + k < K)
@@ -87,29 +90,29 @@ constexpr int kn_cols() {
 // Weight [K][N] (N-contiguous): thread t owns CPT consecutive columns and
 // walks the slice's K range kSkLoads rows at a time, all of a batch's loads
 // issued before any is used; the A rows are restaged in LDS every KC.
-template <typename E>
+template <typename E, int R>
 __global__ __launch_bounds__(kSkThreads) void skinny_kn_partial(
     const E* __restrict__ A, int64_t lda, const int32_t* __restrict__ m_dev, int m_cap, int K,
     int N, int kw, int mm, const E* __restrict__ W, float* __restrict__ part) {
   constexpr int CPT = kn_cols<E>();
   constexpr int KC = kSkKCDown, U = kSkLoads;
   static_assert(KC % U == 0, "whole load batches per chunk");
-  __shared__ __attribute__((aligned(16))) float sA[kSkRows * KC];
+  __shared__ __attribute__((aligned(16))) float sA[R * KC];
   const int M = m_dev != nullptr ? min(*m_dev, m_cap) : m_cap;
-  const int r0 = blockIdx.z * kSkRows;
+  const int r0 = blockIdx.z * R;
   if (r0 >= M) return;
   const int slice = blockIdx.y, kbeg = slice * kw, kfin = min(kbeg + kw, K);
   const int n = (blockIdx.x * kSkThreads + threadIdx.x) * CPT;
   const bool live = n < N;  // N is a multiple of 8: a thread's columns are all in or all out
   const int nc = live ? n : 0;
-  float acc[kSkRows][CPT];
+  float acc[R][CPT];
 #pragma unroll
-  for (int m = 0; m < kSkRows; ++m)
+  for (int m = 0; m < R; ++m)
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[m][c] = 0.f;
   for (int k0 = kbeg; k0 < kfin; k0 += KC) {
     __syncthreads();  // the previous chunk's A is no longer read
-    stage_a<E, KC>(sA, A, lda, r0, M, k0, K);
+    stage_a<E, KC, R>(sA, A, lda, r0, M, k0, K);
     __syncthreads();
     const int kend = min(KC, kfin - k0);
     for (int k = 0; k < kend; k += U) {
@@ -121,7 +124,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kn_partial(
         w[j].load(W + static_cast<int64_t>(k0 + kr) * N + nc);
       }
 #pragma unroll
-      for (int m = 0; m < kSkRows; ++m) {
+      for (int m = 0; m < R; ++m) {
 #pragma unroll
         for (int j4 = 0; j4 < U; j4 += 4) {
           const float4 a = *reinterpret_cast<const float4*>(sA + m * KC + k + j4);
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kn_partial(
   if (!live) return;
   float* dst = part + (static_cast<int64_t>(slice) * mm + r0) * N + n;
 #pragma unroll
-  for (int m = 0; m < kSkRows; ++m)
+  for (int m = 0; m < R; ++m)
     if (r0 + m < M)
 #pragma unroll
       for (int c = 0; c < CPT; ++c) dst[static_cast<int64_t>(m) * N + c] = acc[m][c];
@@ -145,24 +148,24 @@ __global__ __launch_bounds__(kSkThreads) void skinny_kn_partial(
 
 // Weight [N][K] (K-contiguous): thread t owns column n = one weight row and
 // reads the slice's K range 16 bytes at a time, kSkLoads / 2 loads in flight.
-template <typename E>
+template <typename E, int R>
 __global__ __launch_bounds__(kSkThreads) void skinny_nk_partial(
     const E* __restrict__ A, int64_t lda, int M, int K, int N, int kw, int mm,
     const E* __restrict__ W, float* __restrict__ part) {
   constexpr int V = Vec16B<E>::N, KC = kSkKC, U = kSkLoads / 2;
   static_assert(KC % (V * U) == 0, "whole load batches per chunk");
-  __shared__ __attribute__((aligned(16))) float sA[kSkRows * KC];
-  const int r0 = blockIdx.z * kSkRows;
+  __shared__ __attribute__((aligned(16))) float sA[R * KC];
+  const int r0 = blockIdx.z * R;
   const int slice = blockIdx.y, kbeg = slice * kw, kfin = min(kbeg + kw, K);
   const int n = blockIdx.x * kSkThreads + threadIdx.x;
   const bool live = n < N;
-  float acc[kSkRows];
+  float acc[R];
 #pragma unroll
-  for (int m = 0; m < kSkRows; ++m) acc[m] = 0.f;
+  for (int m = 0; m < R; ++m) acc[m] = 0.f;
   const E* wrow = W + static_cast<int64_t>(live ? n : 0) * K;
   for (int k0 = kbeg; k0 < kfin; k0 += KC) {
     __syncthreads();
-    stage_a<E, KC>(sA, A, lda, r0, M, k0, K);
+    stage_a<E, KC, R>(sA, A, lda, r0, M, k0, K);
     __syncthreads();
     const int kend = min(KC, kfin - k0);  // a multiple of V: K is
     for (int k = 0; k < kend; k += V * U) {
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_nk_partial(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int m = 0; m < kSkRows; ++m) {
+        for (int m = 0; m < R; ++m) {
 #pragma unroll
           for (int q = 0; q < V; q += 4) {
             const float4 a = *reinterpret_cast<const float4*>(sA + m * KC + k + u * V + q);
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_nk_partial(
   if (!live) return;
   float* dst = part + (static_cast<int64_t>(slice) * mm + r0) * N + n;
 #pragma unroll
-  for (int m = 0; m < kSkRows; ++m)
+  for (int m = 0; m < R; ++m)
     if (r0 + m < M) dst[static_cast<int64_t>(m) * N] = acc[m];
 }
 
@@ -295,31 +298,55 @@ __global__ __launch_bounds__(kSkThreads) void skinny_up_pack(
 
 int rows_bucket(int64_t m) { return m <= 16 ? 16 : m <= 32 ? 32 : 64; }
 
-hipError_t up_f32(const Geometry& g, const float* x, const float* w_up_t, const float* b_up,
-                  const PackOut& out, float* part, hipStream_t s) {
+template <int R>
+hipError_t up_f32_rows(const Geometry& g, const float* x, const float* w_up_t, const float* b_up,
+                       const PackOut& out, float* part, hipStream_t s) {
   const int M = static_cast<int>(g.n_rows), N = g.d_ff, K = g.d_model;
-  const int nb = (N + kSkThreads - 1) / kSkThreads, nz = (M + kSkRows - 1) / kSkRows;
+  const int nb = (N + kSkThreads - 1) / kSkThreads, nz = (M + R - 1) / R;
   const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkKC, 512);
-  skinny_nk_partial<float><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(x, K, M, K, N, sp.kw,
-                                                                          sp.mm, w_up_t, part);
+  skinny_nk_partial<float, R><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(
+      x, K, M, K, N, sp.kw, sp.mm, w_up_t, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_skinny_up_epilogue<float>(g, sp, part, b_up, out, s);
+}
+
+hipError_t up_f32(const Geometry& g, const float* x, const float* w_up_t, const float* b_up,
+                  const PackOut& out, float* part, hipStream_t s) {
+  const int nb = (g.d_ff + kSkThreads - 1) / kSkThreads;
+  const int nz = static_cast<int>((g.n_rows + kSkRows - 1) / kSkRows);
+  const SkinnySplit sp = skinny_split(g.n_rows, g.d_model, nb * nz, kSkKC, 512);
+  return nb * nz * sp.slices < kSkMinBlocks
+             ? up_f32_rows<kSkRowsSmall>(g, x, w_up_t, b_up, out, part, s)
+             : up_f32_rows<kSkRows>(g, x, w_up_t, b_up, out, part, s);
+}
+
+template <int R>
+hipError_t fallback_f32_rows(const Geometry& g, const float* a, const int32_t* dense_rows,
+                             const int32_t* n_dense, int m_cap, const float* w_down, float* y,
+                             float* part, hipStream_t s) {
+  constexpr int CPT = kn_cols<float>();
+  const int N = g.d_model, K = g.d_ff;
+  const int nb = (N + kSkThreads * CPT - 1) / (kSkThreads * CPT);
+  const int nz = (m_cap + R - 1) / R;
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkKCDown, 512);
+  skinny_kn_partial<float, R><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(
+      a, K, n_dense, m_cap, K, N, sp.kw, sp.mm, w_down, part);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_skinny_fallback_reduce<float>(g, sp, part, n_dense, m_cap, dense_rows, y, s);
 }
 
 hipError_t fallback_f32(const Geometry& g, const float* a, const int32_t* dense_rows,
                         const int32_t* n_dense, int m_cap, const float* w_down, float* y,
                         float* part, hipStream_t s) {
   constexpr int CPT = kn_cols<float>();
-  const int N = g.d_model, K = g.d_ff;
-  const int nb = (N + kSkThreads * CPT - 1) / (kSkThreads * CPT);
+  const int nb = (g.d_model + kSkThreads * CPT - 1) / (kSkThreads * CPT);
   const int nz = (m_cap + kSkRows - 1) / kSkRows;
-  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkKCDown, 512);
-  skinny_kn_partial<float><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(
-      a, K, n_dense, m_cap, K, N, sp.kw, sp.mm, w_down, part);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_skinny_fallback_reduce<float>(g, sp, part, n_dense, m_cap, dense_rows, y, s);
+  const SkinnySplit sp = skinny_split(g.n_rows, g.d_ff, nb * nz, kSkKCDown, 512);
+  return nb * nz * sp.slices < kSkMinBlocks
+             ? fallback_f32_rows<kSkRowsSmall>(g, a, dense_rows, n_dense, m_cap, w_down, y, part, s)
+             : fallback_f32_rows<kSkRows>(g, a, dense_rows, n_dense, m_cap, w_down, y, part, s);
 }
 
 }  // namespace

@@ -353,6 +353,81 @@ __global__ __launch_bounds__(P * kWave) void spmm_split_bf16_kernel(
   }
 }
 
+// Few rows, float32 (or a d_model the XCD-sliced kernel does not take): one
+// workgroup of P waves per (row, chunk of 64 lanes x 16 bytes of columns),
+// wave w gathering tiles [w * tpw, (w + 1) * tpw) of the row; the P partial
+// sums meet in LDS and are added in wave order.
+template <typename E, int P>
+__global__ __launch_bounds__(P * kWave) void spmm_split_kernel(
+    const E* __restrict__ vals, const uint8_t* __restrict__ idx, const uint8_t* __restrict__ cnt,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_dev,
+    const E* __restrict__ w, E* __restrict__ y, int64_t N, int dm, int T, int C, int nt,
+    int n_chunks, int tpw) {
+  constexpr int V = SpmmVec<E>::N;
+  typedef ElemTraits<E> Tr;
+  extern __shared__ uint2 spmm_lists[];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wslots = tpw * C;
+  uint2* list = spmm_lists + wave * wslots;
+  float* red = reinterpret_cast<float*>(spmm_lists + P * wslots);  // [P][V][64]
+  const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
+  const int chunk = blockIdx.y;
+  const int col = chunk * (kWave * V) + lane * V;
+  const bool live_col = col < dm;  // dm is a multiple of 8, so V columns are all in or all out
+  const int t0 = wave * tpw, t1 = min(nt, t0 + tpw);
+  for (int64_t k = blockIdx.x; k < R; k += gridDim.x) {
+    const int64_t n = rows != nullptr ? rows[k] : k;
+    const int64_t s0 = n * nt * C;
+    int nnz = 0;
+    for (int g = t0 * C; g < t1 * C; g += kWave) {
+      const int s = g + lane;
+      bool live = false;
+      uint32_t j = 0;
+      float v = 0.f;
+      if (s < t1 * C) {
+        const int t = s / C;
+        if (s - t * C < static_cast<int>(cnt[n * nt + t])) {
+          const int local = static_cast<int>(idx[s0 + s]);
+          live = local < T;  // a malformed index is ignored rather than read out of bounds
+          j = static_cast<uint32_t>(t * T + local);
+          v = Tr::to_f32(vals[s0 + s]);
+        }
+      }
+      const uint64_t m = wave_ballot(live);
+      if (live) list[nnz + popc_below(m)] = make_uint2(j, __float_as_uint(v));
+      nnz += popc64(m);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's list is in LDS
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int q = 0; q < nnz; q += kListUnroll) {
+      uint2 e[kListUnroll];
+      uint4 wv[kListUnroll];
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u) {
+        e[u] = list[min(q + u, nnz - 1)];  // past the end: reread the last entry, unused
+        wv[u] = live_col ? *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(e[u].x) * dm + col)
+                         : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < kListUnroll; ++u)
+        if (q + u < nnz) fma_row<E>(acc, __uint_as_float(e[u].y), wv[u]);
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) red[(wave * V + i) * kWave + lane] = acc[i];
+    __syncthreads();
+    // wave w finishes columns i = w, w + P, ... of each lane's V
+    for (int i = wave; i < V; i += P) {
+      float sum = 0.f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) sum += red[(p * V + i) * kWave + lane];
+      if (live_col) y[n * dm + col + i] = Tr::from_f32(sum);
+    }
+    __syncthreads();  // red and the lists are reused by the next row
+  }
+}
+
 }  // namespace
 
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
@@ -414,10 +489,37 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
             n_slices);
       return hipGetLastError();
     }
+    {  // few rows, d_model the sliced kernel does not take: split each row over 16 waves
+      constexpr int P = 16;
+      const int tpw = (g.n_tiles + P - 1) / P;
+      const size_t split_bytes = static_cast<size_t>(P) * tpw * g.capacity * 8 +
+                                 static_cast<size_t>(P) * SpmmVec<uint16_t>::N * kWave * 4;
+      if (g.n_rows * n_chunks <= 1024 && split_bytes <= 64 * 1024) {
+        spmm_split_kernel<uint16_t, P><<<dim3(static_cast<unsigned>(g.n_rows), n_chunks),
+                                         P * kWave, split_bytes, s>>>(
+            static_cast<const uint16_t*>(vals), idx, cnt, rows, n_rows_dev,
+            static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y), g.n_rows, g.d_model,
+            g.tile, g.capacity, g.n_tiles, n_chunks, tpw);
+        return hipGetLastError();
+      }
+    }
     spmm_sparse_kernel<uint16_t><<<blocks, kThreads, 0, s>>>(
         static_cast<const uint16_t*>(vals), idx, cnt, rows, n_rows_dev, static_cast<const uint16_t*>(w_down),
         static_cast<uint16_t*>(y), g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles, n_chunks);
   } else {
+    // Few rows: split each row over the 16 waves of a workgroup.
+    constexpr int P = 16;
+    const int tpw = (g.n_tiles + P - 1) / P;
+    const size_t split_bytes = static_cast<size_t>(P) * tpw * g.capacity * 8 +
+                               static_cast<size_t>(P) * SpmmVec<float>::N * kWave * 4;
+    if (g.n_rows * n_chunks <= 1024 && split_bytes <= 64 * 1024) {
+      spmm_split_kernel<float, P><<<dim3(static_cast<unsigned>(g.n_rows), n_chunks), P * kWave,
+                                    split_bytes, s>>>(
+          static_cast<const float*>(vals), idx, cnt, rows, n_rows_dev,
+          static_cast<const float*>(w_down), static_cast<float*>(y), g.n_rows, g.d_model, g.tile,
+          g.capacity, g.n_tiles, n_chunks, tpw);
+      return hipGetLastError();
+    }
     spmm_sparse_kernel<float><<<blocks, kThreads, 0, s>>>(
         static_cast<const float*>(vals), idx, cnt, rows, n_rows_dev, static_cast<const float*>(w_down),
         static_cast<float*>(y), g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles, n_chunks);
