@@ -249,8 +249,8 @@ __device__ __forceinline__ void load_slots(SlotGroup<CC, E>& g, const uint8_t* _
   }
 }
 
-template <typename E, int CC>
-__global__ __launch_bounds__(kRowThreads) void materialize_slots_kernel(
+template <typename E, int CC, int NT>
+__global__ __launch_bounds__(NT) void materialize_slots_kernel(
     int dff, int T, int nt, const int32_t* __restrict__ row_map, const uint8_t* __restrict__ flags,
     const E* __restrict__ spill, E* __restrict__ vals, uint8_t* __restrict__ idx,
     uint8_t* __restrict__ cnt, E* __restrict__ dense_values, int64_t cap) {
@@ -261,13 +261,13 @@ __global__ __launch_bounds__(kRowThreads) void materialize_slots_kernel(
   const int64_t slot0 = n * nt;
   if (m < cap) {
     E* dst = dense_values + static_cast<int64_t>(m) * dff;
-    for (int base = threadIdx.x * V; base < dff; base += B * kRowThreads * V) {
+    for (int base = threadIdx.x * V; base < dff; base += B * NT * V) {
       int t[B], count[B];
       uint8_t f[B];
       SlotGroup<CC, E> sg[B];
 #pragma unroll
       for (int j = 0; j < B; ++j) {
-        const int c = min(base + j * kRowThreads * V, dff - V);  // past the end: reread, unused
+        const int c = min(base + j * NT * V, dff - V);  // past the end: reread, unused
         t[j] = c / T;
         f[j] = flags[slot0 + t[j]];
         count[j] = cnt[slot0 + t[j]];
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kRowThreads) void materialize_slots_kernel(
       }
 #pragma unroll
       for (int j = 0; j < B; ++j) {
-        const int c = base + j * kRowThreads * V;
+        const int c = base + j * NT * V;
         if (c >= dff) break;
         Vec16<E> o;
         if (f[j]) {
@@ -296,11 +296,11 @@ __global__ __launch_bounds__(kRowThreads) void materialize_slots_kernel(
   }
   __syncthreads();  // every read of this row's slots is done before they are cleared
   const int nslots = nt * CC;
-  for (int i = threadIdx.x; i < nslots; i += kRowThreads) {
+  for (int i = threadIdx.x; i < nslots; i += NT) {
     vals[slot0 * CC + i] = E(0);
     idx[slot0 * CC + i] = 0;
   }
-  for (int i = threadIdx.x; i < nt; i += kRowThreads) cnt[slot0 + i] = 0;
+  for (int i = threadIdx.x; i < nt; i += NT) cnt[slot0 + i] = 0;
 }
 
 // One wave per (row, tile) of an existing h.
@@ -393,11 +393,18 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   // rebuild each 16-byte piece in registers from the slot groups (75
   // against 108 us for 4750 rows of 28 KB).
   if (full_src == nullptr && (g.capacity == 4 || g.capacity == 8) && row_bytes > 20 * 1024) {
+    // A few rows (decode-sized batches) are latency-bound: 1024 threads per
+    // row then rebuild a row in one batch of loads instead of several.
     auto run = [&](auto tag, auto cc) {
       typedef decltype(tag) E;
-      materialize_slots_kernel<E, decltype(cc)::value><<<blocks, kRowThreads, 0, s>>>(
-          g.d_ff, g.tile, g.n_tiles, row_map, flags, static_cast<const E*>(spill),
-          static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap);
+      if (g.n_rows <= kSkinnyMaxRows)
+        materialize_slots_kernel<E, decltype(cc)::value, 1024><<<blocks, 1024, 0, s>>>(
+            g.d_ff, g.tile, g.n_tiles, row_map, flags, static_cast<const E*>(spill),
+            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap);
+      else
+        materialize_slots_kernel<E, decltype(cc)::value, kRowThreads><<<blocks, kRowThreads, 0, s>>>(
+            g.d_ff, g.tile, g.n_tiles, row_map, flags, static_cast<const E*>(spill),
+            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap);
     };
     typedef std::integral_constant<int, 4> C4;
     typedef std::integral_constant<int, 8> C8;
