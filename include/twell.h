@@ -74,7 +74,7 @@ extern "C" {
 typedef enum twell_status {
   TWELL_OK = 0,
   TWELL_ERR_INVALID_ARG = -1,    /* null pointer, negative size, bad geometry */
-  TWELL_ERR_UNSUPPORTED = -2,    /* valid TwELL geometry this build has no kernel for */
+  TWELL_ERR_UNSUPPORTED = -2,    /* valid TwELL geometry the library has no kernel for */
   TWELL_ERR_WORKSPACE = -3,      /* workspace smaller than the *_workspace_size query */
   TWELL_ERR_HIP = -4,            /* a HIP launch failed */
   TWELL_ERR_DENSE_CAPACITY = -5  /* device-side: more dense rows than dense_capacity */
