@@ -227,6 +227,23 @@ def test_forward_small(name, n, dm, dff):
     np.testing.assert_array_equal(u32(as_f32(out2.hybrid.values)), u32(as_f32(out.hybrid.values)))
 
 
+@pytest.mark.parametrize("C", [5, 8, 16, 64, 128])
+def test_forward_capacities(C):
+    """The 1B layer's tile width with other capacities (the capacity sweep):
+    staged and unstaged pack epilogues, slot lists in LDS or not, C = T."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=300, d_model=256, d_ff=1024, capacity=C)
+    say(f"forward capacity {C}")
+    t = make_inputs(cfg)
+    t["b_up"] = t["b_up"] + 1.2  # ~10% active: some tiles overflow even at larger C
+    out = run_forward(cfg, t)
+    assert int(out.status.item()) == twell.TWELL_OK
+    h_ref, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    tol = TOL[cfg.torch_dtype]
+    assert_close_rel(as_f64(out.h_debug), h_ref, tol, "h")
+    assert_pack_matches(out.hybrid, as_f32(out.h_debug))
+    assert_close_rel(as_f64(out.y), y_ref, tol, "y")
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_forward_bias_limits(dtype):
     cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=150, d_model=128, d_ff=512, dtype=dtype)
