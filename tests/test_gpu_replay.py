@@ -1,7 +1,8 @@
-"""ffn_sparse_forward captured into a HIP graph: every replay equals the eager
-call bit for bit, with eager work and synchronisations between replays.  The
-capture includes the library's fork onto its auxiliary stream and the join
-back (events), and, at 16 rows, the split-K path."""
+"""Stream ordering of ffn_sparse_forward.  Captured into a HIP graph, every
+replay equals the eager call bit for bit, with eager work and
+synchronisations between replays (the capture includes the library's fork
+onto its auxiliary stream and the join back, and, at 16 rows, the split-K
+path); queued back to back on shared buffers, calls do not overlap."""
 import numpy as np
 import pytest
 import torch
@@ -49,3 +50,32 @@ def test_graph_replays_match_eager(name, n, dm, dff):
         for a, b in zip(got, ref):
             np.testing.assert_array_equal(a, b)
     del g
+
+
+def test_back_to_back_calls_on_shared_buffers():
+    """Forward calls queued back to back on one stream, alternating two inputs
+    and reusing the same output and workspace buffers, with no host
+    synchronisation in between: each call's sparse product (on the auxiliary
+    stream) must finish before the next call reuses the buffers.  The final
+    outputs equal a lone call's, bit for bit."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=600, d_model=512, d_ff=2048)
+    da = inputs_to_device(make_inputs(cfg))
+    db = inputs_to_device(make_inputs(cfg.replace(seed=1)))
+    bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
+                                 cfg.torch_dtype, torch.device("cuda:0"))
+    run = lambda d: twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"],
+                                             cfg.tile, cfg.capacity, out=bufs)
+    refs = {}
+    for name, d in (("a", da), ("b", db)):
+        run(d)
+        torch.cuda.synchronize()
+        refs[name] = snapshot(bufs)
+    assert not np.array_equal(refs["a"][0], refs["b"][0])
+    for last in ("a", "b"):
+        for i in range(40):
+            run(db if (i % 2 == 0) == (last == "a") else da)
+        run(da if last == "a" else db)
+        torch.cuda.synchronize()
+        got = snapshot(bufs)
+        for x, y in zip(got, refs[last]):
+            np.testing.assert_array_equal(x, y)
