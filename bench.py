@@ -169,6 +169,104 @@ def time_secondary(cfg, steps, warmup, flush, dev):
     return out
 
 
+# The conversions (dense_to_twell = twell_pack, twell_to_dense = twell_unpack)
+# are timed on the h of the 16384-token layer (d_ff 28672, T 256, C 8, ~13%
+# active), where they move the most bytes, beside that layer's forward.
+CONVERSION_WORKLOAD = "large_bf16"
+PACK_KERNELS = "pack_tiles_kernel + row_or_kernel + route_scan_kernel + materialize_kernel"
+UNPACK_KERNELS = "unpack_kernel"
+
+
+def _timed_calls(fn, steps, warmup, flush):
+    """Mean ms of fn() over `steps` cold-cache calls, an event pair around each."""
+    for i in range(warmup):
+        flush_cache(flush, i)
+        fn()
+    torch.cuda.synchronize()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for i in range(steps):
+        flush_cache(flush, i)
+        pairs[i][0].record()
+        fn()
+        pairs[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def conversion_bytes(n_rows, d_ff, tile, capacity, elem_bytes, n_dense):
+    """Algorithmic HBM bytes of one conversion: the dense h [N, d_ff] once,
+    the TwELL arrays (values, indices, counts) once and the dense rows once
+    (read for twell_pack's input and written as its output, or the reverse
+    for twell_unpack)."""
+    nt = d_ff // tile
+    twell_bytes = n_rows * nt * (capacity * elem_bytes + capacity + 1)
+    return n_rows * d_ff * elem_bytes + twell_bytes + n_dense * d_ff * elem_bytes
+
+
+def time_conversions(cfg, steps, warmup, flush, dev):
+    """twell_pack and twell_unpack on the layer's own h, plus its forward."""
+    t = make_inputs(cfg)
+    d = {k: v.to(dev) for k, v in t.items()}
+    del t
+    e = torch.tensor([], dtype=cfg.torch_dtype).element_size()
+    # h exactly as the forward packs it (the debug copy written from the same registers)
+    hb = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
+                               cfg.torch_dtype, dev, debug_h=True)
+    twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile, cfg.capacity,
+                             out=hb, debug_h=True)
+    torch.cuda.synchronize()
+    h = hb.h_debug
+    del hb
+    torch.cuda.empty_cache()
+    # the layer's forward (plain calls) and its dense FFN, as for the other layers
+    bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
+                                 cfg.torch_dtype, dev)
+    total, _, _, _ = time_forward(cfg, d, bufs, steps, warmup, flush)
+    if int(bufs.status.item()) != twell.TWELL_OK:
+        raise RuntimeError("forward of the conversion layer reported an error status")
+    dense = time_dense(d, steps, warmup, flush)
+    del bufs
+    del d
+    torch.cuda.empty_cache()
+    shape = twell.make_shape(cfg.n_rows, 8, cfg.d_ff, cfg.tile, cfg.capacity, cfg.torch_dtype)
+    hy = twell.Hybrid.empty(cfg.n_rows, cfg.d_ff, cfg.tile, cfg.capacity, cfg.torch_dtype, dev)
+    ws = torch.empty((max(twell.pack_workspace_bytes(shape), 1),), dtype=torch.uint8, device=dev)
+    st = torch.empty((1,), dtype=torch.int32, device=dev)
+    pack_ms = _timed_calls(lambda: twell.twell_pack(h, cfg.tile, cfg.capacity, out=hy,
+                                                    workspace=ws, status=st),
+                           steps, warmup, flush)
+    if int(st.item()) != twell.TWELL_OK:
+        raise RuntimeError("twell_pack reported an error status")
+    back = torch.empty_like(h)
+    unpack_ms = _timed_calls(lambda: twell.twell_unpack(hy, out=back), steps, warmup, flush)
+    torch.cuda.synchronize()
+    if not torch.equal(back.view(torch.int16), h.view(torch.int16)):
+        raise RuntimeError("twell_unpack(twell_pack(h)) differs from h")
+    n_dense = hy.n_dense_host()
+    nbytes = conversion_bytes(cfg.n_rows, cfg.d_ff, cfg.tile, cfg.capacity, e, n_dense)
+
+    def stage(ms_list, kernels):
+        ms = float(np.mean(ms_list))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"ms": ms, "ms_p10": percentile(ms_list, 10), "ms_p90": percentile(ms_list, 90),
+                "bound": "hbm", "bytes_per_launch": nbytes, "achieved": gbs, "unit": "GB/s",
+                "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                "kernels": kernels}
+
+    fms, dms = float(np.mean(total)), float(np.mean(dense))
+    out = {"workload": cfg.name, "n_rows": cfg.n_rows, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+           "tile": cfg.tile, "capacity": cfg.capacity, "n_dense": n_dense,
+           "twell_pack": stage(pack_ms, PACK_KERNELS),
+           "twell_unpack": stage(unpack_ms, UNPACK_KERNELS),
+           "roundtrip_bitwise_equal": True,
+           "forward_ms": fms, "tokens_per_s": cfg.n_rows / (fms * 1e-3),
+           "dense_bf16_ffn_ms": dms, "speedup_twell_over_dense": dms / fms}
+    del h, hy, ws, back
+    torch.cuda.empty_cache()
+    return out
+
+
 def source_sha(stage: str) -> str:
     h = hashlib.sha256()
     for f in STAGE_SOURCES[stage]:
@@ -270,6 +368,8 @@ def main(argv=None):
     ap.add_argument("--no-dense-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the second (decode-sized) layer timed beside the headline one")
+    ap.add_argument("--no-conversions", action="store_true",
+                    help="skip twell_pack / twell_unpack and the forward on the 16384-token layer")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer's multi-GPU "
@@ -397,6 +497,13 @@ def main(argv=None):
         torch.cuda.empty_cache()
         result["secondary"] = time_secondary(CONFIGS[SECONDARY_WORKLOAD], args.steps, args.warmup,
                                              flush, dev)
+    if not args.no_conversions:
+        log(f"[bench] conversions on {CONVERSION_WORKLOAD}")
+        if "d" in locals():
+            del d, bufs
+        torch.cuda.empty_cache()
+        result["conversions"] = time_conversions(CONFIGS[CONVERSION_WORKLOAD], args.steps,
+                                                 args.warmup, flush, dev)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle on a sample of rows")
         result["cpu_baseline"] = cpu_oracle_baseline(t, cfg)

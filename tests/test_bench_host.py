@@ -37,3 +37,11 @@ def test_stage_sources_exist():
         for f in files:
             assert os.path.exists(os.path.join(bench.ROOT, f)), (stage, f)
         assert len(bench.source_sha(stage)) == 16
+
+
+def test_conversion_bytes_counts_h_twell_and_dense_rows_once():
+    # 2 rows of d_ff 512 in bf16, T 256 (2 tiles), C 8, one dense row:
+    # h 2*512*2 = 2048; TwELL 2 rows * 2 tiles * (8*2 + 8 + 1) = 100; dense row 512*2 = 1024
+    assert bench.conversion_bytes(2, 512, 256, 8, 2, 1) == 2048 + 100 + 1024
+    # no dense rows, fp32, T = C = 64: h 64*4, TwELL 1 tile * (64*4 + 64 + 1)
+    assert bench.conversion_bytes(1, 64, 64, 64, 4, 0) == 256 + 321
