@@ -202,12 +202,11 @@ __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
       }
       __syncthreads();
       for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
-        Vec16<E> o;
-        if (flags[slot0 + c / T])
-          load_vec(o, spill + n * dff + c);
-        else
-          load_vec(o, rowbuf + c);
-        store_vec(dst + c, o);
+        // a plain 16-byte value (an array loaded from either address space
+        // would be kept in scratch memory)
+        const uint4 o = flags[slot0 + c / T] ? *reinterpret_cast<const uint4*>(spill + n * dff + c)
+                                             : *reinterpret_cast<const uint4*>(rowbuf + c);
+        *reinterpret_cast<uint4*>(dst + c) = o;
       }
     }
   }

@@ -88,6 +88,22 @@ def test_pack_dense_capacity_exceeded():
     np.testing.assert_array_equal(u32(as_f32(hy.values)), u32(ref.values))
 
 
+@pytest.mark.parametrize("dtype,dff", [("fp32", 16384), ("bf16", 32768)])
+def test_pack_long_rows_two_pass(dtype, dff):
+    """Rows of 64 KB: the dense rows are copied straight from h, with no row
+    buffer in LDS."""
+    say(f"pack long rows {dtype} dff={dff}")
+    ht, hh = sparse_h(31, 37, dff, 0.01, DT[dtype])
+    hy, status = twell.twell_pack(ht.cuda(), 256, 8)
+    torch.cuda.synchronize()
+    assert int(status.item()) == twell.TWELL_OK
+    ref = assert_pack_matches(hy, hh)
+    assert 0 < ref.n_dense < 37
+    u = twell.twell_unpack(hy)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(u32(as_f32(u)), u32(oracle.unpack(ref)))
+
+
 def test_pack_zero_rows():
     h = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     hy, status = twell.twell_pack(h, 128, 4)
