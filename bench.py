@@ -170,8 +170,11 @@ def time_secondary(cfg, steps, warmup, flush, dev):
 
 
 # The conversions (dense_to_twell = twell_pack, twell_to_dense = twell_unpack)
-# are timed on the h of the 16384-token layer (d_ff 28672, T 256, C 8, ~13%
-# active), where they move the most bytes, beside that layer's forward.
+# are timed on an h of the 16384-token layer (d_ff 28672, T 256, C 8, ~13%
+# active), where they move the most bytes.  That h is made by torch from the
+# layer's own inputs (ReLU(x W_up^T + b) in bf16): the sparse forward's kernels
+# then run on the headline layer only, so their per-kernel profile averages
+# are the headline's.
 CONVERSION_WORKLOAD = "large_bf16"
 PACK_KERNELS = "pack_tiles_kernel + row_or_kernel + route_scan_kernel + materialize_kernel"
 UNPACK_KERNELS = "unpack_kernel"
@@ -205,30 +208,16 @@ def conversion_bytes(n_rows, d_ff, tile, capacity, elem_bytes, n_dense):
 
 
 def time_conversions(cfg, steps, warmup, flush, dev):
-    """twell_pack and twell_unpack on the layer's own h, plus its forward."""
+    """twell_pack and twell_unpack on an h of the layer, cold cache."""
     t = make_inputs(cfg)
-    d = {k: v.to(dev) for k, v in t.items()}
+    x, w_up_t = t["x"].to(dev), t["w_up_t"].to(dev)
+    b16 = t["b_up"].to(dev).to(cfg.torch_dtype)
     del t
-    e = torch.tensor([], dtype=cfg.torch_dtype).element_size()
-    # h exactly as the forward packs it (the debug copy written from the same registers)
-    hb = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
-                               cfg.torch_dtype, dev, debug_h=True)
-    twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile, cfg.capacity,
-                             out=hb, debug_h=True)
+    h = torch.relu(torch.nn.functional.linear(x, w_up_t, b16))
+    del x, w_up_t, b16
     torch.cuda.synchronize()
-    h = hb.h_debug
-    del hb
     torch.cuda.empty_cache()
-    # the layer's forward (plain calls) and its dense FFN, as for the other layers
-    bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
-                                 cfg.torch_dtype, dev)
-    total, _, _, _ = time_forward(cfg, d, bufs, steps, warmup, flush)
-    if int(bufs.status.item()) != twell.TWELL_OK:
-        raise RuntimeError("forward of the conversion layer reported an error status")
-    dense = time_dense(d, steps, warmup, flush)
-    del bufs
-    del d
-    torch.cuda.empty_cache()
+    e = h.element_size()
     shape = twell.make_shape(cfg.n_rows, 8, cfg.d_ff, cfg.tile, cfg.capacity, cfg.torch_dtype)
     hy = twell.Hybrid.empty(cfg.n_rows, cfg.d_ff, cfg.tile, cfg.capacity, cfg.torch_dtype, dev)
     ws = torch.empty((max(twell.pack_workspace_bytes(shape), 1),), dtype=torch.uint8, device=dev)
@@ -244,6 +233,7 @@ def time_conversions(cfg, steps, warmup, flush, dev):
     if not torch.equal(back.view(torch.int16), h.view(torch.int16)):
         raise RuntimeError("twell_unpack(twell_pack(h)) differs from h")
     n_dense = hy.n_dense_host()
+    nnz = int(torch.count_nonzero(h).item())
     nbytes = conversion_bytes(cfg.n_rows, cfg.d_ff, cfg.tile, cfg.capacity, e, n_dense)
 
     def stage(ms_list, kernels):
@@ -254,14 +244,12 @@ def time_conversions(cfg, steps, warmup, flush, dev):
                 "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                 "kernels": kernels}
 
-    fms, dms = float(np.mean(total)), float(np.mean(dense))
-    out = {"workload": cfg.name, "n_rows": cfg.n_rows, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
-           "tile": cfg.tile, "capacity": cfg.capacity, "n_dense": n_dense,
+    out = {"workload": cfg.name, "n_rows": cfg.n_rows, "d_ff": cfg.d_ff, "tile": cfg.tile,
+           "capacity": cfg.capacity, "h": "ReLU(x W_up^T + b) of the layer's inputs, torch bf16",
+           "active_fraction": nnz / (cfg.n_rows * cfg.d_ff), "n_dense": n_dense,
            "twell_pack": stage(pack_ms, PACK_KERNELS),
            "twell_unpack": stage(unpack_ms, UNPACK_KERNELS),
-           "roundtrip_bitwise_equal": True,
-           "forward_ms": fms, "tokens_per_s": cfg.n_rows / (fms * 1e-3),
-           "dense_bf16_ffn_ms": dms, "speedup_twell_over_dense": dms / fms}
+           "roundtrip_bitwise_equal": True}
     del h, hy, ws, back
     torch.cuda.empty_cache()
     return out
@@ -369,7 +357,7 @@ def main(argv=None):
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the second (decode-sized) layer timed beside the headline one")
     ap.add_argument("--no-conversions", action="store_true",
-                    help="skip twell_pack / twell_unpack and the forward on the 16384-token layer")
+                    help="skip twell_pack / twell_unpack on the 16384-token layer's h")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer's multi-GPU "
