@@ -77,3 +77,47 @@ def test_full_size_forward(name):
     assert_close_rel(h_rows.astype(np.float64), h_ref, tol, "h")
     err, scale = assert_close_rel(as_f64(out.y[sel]), y_ref, tol, "y")
     say(f"  y max|err| {err:.3e} vs tol*max|y| {tol * scale:.3e}")
+
+
+def test_full_size_conversions():
+    """twell_pack / twell_unpack at the 16384-token layer (the size bench.py
+    times them at) on the GPU's own h: the standalone pack equals the
+    forward's fused pack bit for bit on every row, sampled rows equal the
+    oracle's packer, and unpack(pack(h)) == h bitwise on every row."""
+    cfg = CONFIGS["large_bf16"]
+    say("full-size conversions: generating inputs")
+    t = make_inputs(cfg)
+    d = {k: v.cuda() for k, v in t.items()}
+    del t
+    say("full-size conversions: forward (h and its fused pack)")
+    out = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
+                                   cfg.capacity, debug_h=True)
+    del d
+    torch.cuda.synchronize()
+    assert int(out.status.item()) == twell.TWELL_OK
+    h, fused = out.h_debug, out.hybrid
+    say("full-size conversions: twell_pack")
+    hy, status = twell.twell_pack(h, cfg.tile, cfg.capacity)
+    torch.cuda.synchronize()
+    assert int(status.item()) == twell.TWELL_OK
+    n_dense = hy.n_dense_host()
+    assert n_dense == fused.n_dense_host() and 0 < n_dense < cfg.n_rows
+    say(f"  n_dense = {n_dense} of {cfg.n_rows}")
+    assert torch.equal(hy.counts, fused.counts)
+    assert torch.equal(hy.indices, fused.indices)
+    assert torch.equal(hy.values.view(torch.int16), fused.values.view(torch.int16))
+    assert torch.equal(hy.dense_rows[:n_dense], fused.dense_rows[:n_dense])
+    assert torch.equal(hy.dense_values[:n_dense].view(torch.int16),
+                       fused.dense_values[:n_dense].view(torch.int16))
+    rng = np.random.default_rng(99)
+    rows = np.sort(rng.choice(cfg.n_rows, size=16, replace=False))
+    sel = torch.as_tensor(rows, device="cuda")
+    ref = oracle.pack(as_f32(h[sel]), cfg.tile, cfg.capacity)
+    np.testing.assert_array_equal(hy.counts[sel].cpu().numpy(), ref.counts)
+    np.testing.assert_array_equal(hy.indices[sel].cpu().numpy(), ref.indices)
+    np.testing.assert_array_equal(u32(as_f32(hy.values[sel])), u32(ref.values))
+    say("full-size conversions: twell_unpack")
+    del out, fused
+    u = twell.twell_unpack(hy)
+    torch.cuda.synchronize()
+    assert torch.equal(u.view(torch.int16), h.view(torch.int16))
