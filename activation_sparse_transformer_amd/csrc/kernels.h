@@ -88,10 +88,32 @@ hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* de
 // G2b: dense_values[m] = row n of h (from `full_src` if given, else from the
 // TwELL slots of the row plus the spilled overflowing tiles), then the row's
 // TwELL slots are cleared.
+// Routing outputs written by a dense-row build that routes the rows itself.
+struct RouteOut {
+  int64_t n_rows;
+  int32_t* dense_rows;
+  int32_t* n_dense;
+  int32_t* sparse_rows;
+  int32_t* n_sparse;
+  int32_t* status;
+};
+
 hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* row_map,
                               const uint8_t* flags, const void* spill, const void* full_src,
                               void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
-                              int64_t dense_cap, hipStream_t s);
+                              int64_t dense_cap, hipStream_t s, const RouteOut* route = nullptr);
+
+// G2a + G2b in one launch for batches of at most 64 rows whose dense rows are
+// rebuilt from 4 or 8 slots per tile (rows over 20 KB): each row's workgroup
+// ORs every row's tile flags itself and numbers the dense rows with one
+// ballot; writes what launch_route_scan and launch_materialize write, except
+// row_dense and row_map.  `materialize_routes_itself` says when it applies
+// (from_slots: the rows come from the forward's slots and spill, not from h).
+bool materialize_routes_itself(const Geometry& g, int elem_bytes, bool from_slots);
+hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const RouteBufs& rb,
+                                    const void* spill, void* vals, uint8_t* idx, uint8_t* cnt,
+                                    int32_t* dense_rows, void* dense_values, int64_t dense_cap,
+                                    int32_t* n_dense, int32_t* status, hipStream_t s);
 
 // G6: twell_to_dense.
 hipError_t launch_unpack(const Geometry& g, int elem_bytes, const void* vals, const uint8_t* idx,

@@ -248,14 +248,56 @@ __device__ __forceinline__ void load_slots(SlotGroup<CC, E>& g, const uint8_t* _
   }
 }
 
-template <typename E, int CC, int NT>
+// Rows routed by the scan (row_map), or, with ROUTE (at most 64 rows, one
+// workgroup per row), by the kernel itself: every workgroup ORs the tile
+// flags of all rows into LDS, one ballot over the rows gives each dense row
+// its index (dense rows below it, so ascending token order), and workgroup
+// 0 writes the dense-row list, the sparse-row list, their counts and the
+// status word, as the scan would.
+template <typename E, int CC, int NT, bool ROUTE>
 __global__ __launch_bounds__(NT) void materialize_slots_kernel(
     int dff, int T, int nt, const int32_t* __restrict__ row_map, const uint8_t* __restrict__ flags,
     const E* __restrict__ spill, E* __restrict__ vals, uint8_t* __restrict__ idx,
-    uint8_t* __restrict__ cnt, E* __restrict__ dense_values, int64_t cap) {
+    uint8_t* __restrict__ cnt, E* __restrict__ dense_values, int64_t cap, RouteOut ro) {
   constexpr int V = Vec16<E>::N, B = 4;
   const int64_t n = blockIdx.x;
-  const int m = row_map[n];
+  int m;
+  if constexpr (ROUTE) {
+    static_assert(NT >= kWave, "one full wave for the row ballot");
+    __shared__ uint8_t s_rd[kWave];
+    __shared__ uint64_t s_mask;
+    const int N = static_cast<int>(ro.n_rows);  // at most 64
+    if (threadIdx.x < kWave) s_rd[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < N * nt; i += NT)
+      if (flags[i]) s_rd[i / nt] = 1;  // every writer stores 1
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      const int r = threadIdx.x;
+      const bool d = r < N && s_rd[r] != 0;
+      const uint64_t mask = wave_ballot(d);
+      if (r == 0) s_mask = mask;
+      if (n == 0 && r < N) {
+        const int below = popc_below(mask);  // dense rows below row r
+        if (d) {
+          if (below < cap) ro.dense_rows[below] = r;
+        } else {
+          ro.sparse_rows[r - below] = r;
+        }
+        if (r == 0) {
+          const int total = popc64(mask);
+          *ro.n_dense = total;
+          *ro.n_sparse = N - total;
+          if (ro.status != nullptr) *ro.status = total > cap ? TWELL_ERR_DENSE_CAPACITY : TWELL_OK;
+        }
+      }
+    }
+    __syncthreads();
+    const uint64_t mask = s_mask;
+    m = ((mask >> n) & 1u) ? popc64(mask & ((uint64_t{1} << n) - 1u)) : -1;
+  } else {
+    m = row_map[n];
+  }
   if (m < 0) return;
   const int64_t slot0 = n * nt;
   if (m < cap) {
@@ -380,10 +422,26 @@ hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* de
   return hipGetLastError();
 }
 
+bool materialize_routes_itself(const Geometry& g, int elem_bytes, bool from_slots) {
+  const size_t row_bytes = static_cast<size_t>(g.d_ff) * elem_bytes;
+  return from_slots && g.n_rows > 0 && g.n_rows <= kSkinnyMaxRows &&
+         (g.capacity == 4 || g.capacity == 8) && row_bytes > 20 * 1024;
+}
+
+hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const RouteBufs& rb,
+                                    const void* spill, void* vals, uint8_t* idx, uint8_t* cnt,
+                                    int32_t* dense_rows, void* dense_values, int64_t dense_cap,
+                                    int32_t* n_dense, int32_t* status, hipStream_t s) {
+  if (!materialize_routes_itself(g, elem_bytes, true)) return hipErrorInvalidValue;
+  const RouteOut ro{g.n_rows, dense_rows, n_dense, rb.sparse_rows, rb.n_sparse, status};
+  return launch_materialize(g, elem_bytes, nullptr, rb.flags, spill, nullptr, vals, idx, cnt,
+                            dense_values, dense_cap, s, &ro);
+}
+
 hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* row_map,
                               const uint8_t* flags, const void* spill, const void* full_src,
                               void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
-                              int64_t dense_cap, hipStream_t s) {
+                              int64_t dense_cap, hipStream_t s, const RouteOut* route) {
   if (g.n_rows == 0) return hipSuccess;
   const unsigned blocks = static_cast<unsigned>(g.n_rows);
   const size_t row_bytes = static_cast<size_t>(g.d_ff) * elem_bytes;
@@ -396,14 +454,20 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
     // row then rebuild a row in one batch of loads instead of several.
     auto run = [&](auto tag, auto cc) {
       typedef decltype(tag) E;
-      if (g.n_rows <= kSkinnyMaxRows)
-        materialize_slots_kernel<E, decltype(cc)::value, 1024><<<blocks, 1024, 0, s>>>(
+      if (g.n_rows <= kSkinnyMaxRows && route != nullptr)
+        materialize_slots_kernel<E, decltype(cc)::value, 1024, true><<<blocks, 1024, 0, s>>>(
+            g.d_ff, g.tile, g.n_tiles, nullptr, flags, static_cast<const E*>(spill),
+            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap, *route);
+      else if (g.n_rows <= kSkinnyMaxRows)
+        materialize_slots_kernel<E, decltype(cc)::value, 1024, false><<<blocks, 1024, 0, s>>>(
             g.d_ff, g.tile, g.n_tiles, row_map, flags, static_cast<const E*>(spill),
-            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap);
+            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap, RouteOut{});
       else
-        materialize_slots_kernel<E, decltype(cc)::value, kRowThreads><<<blocks, kRowThreads, 0, s>>>(
-            g.d_ff, g.tile, g.n_tiles, row_map, flags, static_cast<const E*>(spill),
-            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap);
+        materialize_slots_kernel<E, decltype(cc)::value, kRowThreads, false>
+            <<<blocks, kRowThreads, 0, s>>>(g.d_ff, g.tile, g.n_tiles, row_map, flags,
+                                            static_cast<const E*>(spill), static_cast<E*>(vals),
+                                            idx, cnt, static_cast<E*>(dense_values), dense_cap,
+                                            RouteOut{});
     };
     typedef std::integral_constant<int, 4> C4;
     typedef std::integral_constant<int, 8> C8;

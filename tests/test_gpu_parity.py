@@ -210,8 +210,11 @@ SMALL = [
     # a float32 row longer than 64 KB: dense rows rebuilt without the LDS row buffer
     ("tiny_fp32", 20, 64, 16448),
     # bf16 rows over 20 KB with 4 or 8 slots per tile: dense rows rebuilt from slot groups
+    # (at most 64 rows: the build routes the rows itself)
     ("ffn_1b_bf16", 70, 128, 10368),
     ("large_bf16", 33, 64, 10752),
+    ("ffn_1b_bf16", 64, 192, 10368),
+    ("decode_bf16", 1, 128, 12288),
 ]
 
 
@@ -276,13 +279,14 @@ def test_forward_bias_limits(dtype):
     assert_close_rel(as_f64(out.y), y_ref, TOL[cfg.torch_dtype])
 
 
-@pytest.mark.parametrize("n_rows", [200, 1500])
-def test_forward_dense_capacity_exceeded(n_rows):
+@pytest.mark.parametrize("n_rows,d_ff", [(200, 1024), (1500, 1024), (48, 12288)])
+def test_forward_dense_capacity_exceeded(n_rows, d_ff):
     """Too many dense rows: the status says so, n_dense is the true count and
     the first dense_capacity dense rows are stored, whether the capacity runs
     out early or at the last dense row, with the row flags ORed inside the
-    scan (200 rows) or by the separate row pass (1500 rows)."""
-    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=128, d_ff=1024)
+    scan (200 rows), by the separate row pass (1500 rows), or by the dense-row
+    build itself (48 rows of 24 KB)."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=128, d_ff=d_ff)
     t = make_inputs(cfg)
     total = run_forward(cfg, t).hybrid.n_dense_host()
     for cap in (3, total - 1):
