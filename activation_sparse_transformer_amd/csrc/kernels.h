@@ -103,12 +103,12 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
                               void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
                               int64_t dense_cap, hipStream_t s, const RouteOut* route = nullptr);
 
-// G2a + G2b in one launch for batches of at most 64 rows whose dense rows are
-// rebuilt from 4 or 8 slots per tile (rows over 20 KB): each row's workgroup
-// ORs every row's tile flags itself and numbers the dense rows with one
-// ballot; writes what launch_route_scan and launch_materialize write, except
-// row_dense and row_map.  `materialize_routes_itself` says when it applies
-// (from_slots: the rows come from the forward's slots and spill, not from h).
+// G2a + G2b in one launch for batches of at most 64 rows: each row's
+// workgroup of the dense-row build ORs every row's tile flags itself and
+// numbers the dense rows with one ballot; writes what launch_route_scan and
+// launch_materialize write, except row_dense and row_map.
+// `materialize_routes_itself` says when it applies (from_slots: the rows come
+// from the forward's slots and spill, not from h).
 bool materialize_routes_itself(const Geometry& g, int elem_bytes, bool from_slots);
 hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const RouteBufs& rb,
                                     const void* spill, void* vals, uint8_t* idx, uint8_t* cnt,

@@ -146,21 +146,62 @@ __device__ __forceinline__ void gather_tile_vec(Vec16<E>& out, const E* __restri
   }
 }
 
+// Routing of at most 64 rows inside a workgroup of at least 64 threads:
+// every workgroup ORs the tile flags of all rows into LDS, and one ballot over
+// the rows gives each dense row its index (dense rows below it, so ascending
+// token order).  Workgroup 0 also writes the dense-row list, the sparse-row
+// list, their counts and the status word, as the scan would.  Returns the
+// dense index of row n, or -1 for a sparse row.
+__device__ int route_rows_in_block(const RouteOut& ro, const uint8_t* __restrict__ flags, int nt,
+                                   int64_t cap, int64_t n) {
+  __shared__ uint8_t s_rd[kWave];
+  __shared__ uint64_t s_mask;
+  const int N = static_cast<int>(ro.n_rows);  // at most 64
+  if (threadIdx.x < kWave) s_rd[threadIdx.x] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < N * nt; i += blockDim.x)
+    if (flags[i]) s_rd[i / nt] = 1;  // every writer stores 1
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int r = threadIdx.x;
+    const bool d = r < N && s_rd[r] != 0;
+    const uint64_t mask = wave_ballot(d);
+    if (r == 0) s_mask = mask;
+    if (n == 0 && r < N) {
+      const int below = popc_below(mask);  // dense rows below row r
+      if (d) {
+        if (below < cap) ro.dense_rows[below] = r;
+      } else {
+        ro.sparse_rows[r - below] = r;
+      }
+      if (r == 0) {
+        const int total = popc64(mask);
+        *ro.n_dense = total;
+        *ro.n_sparse = N - total;
+        if (ro.status != nullptr) *ro.status = total > cap ? TWELL_ERR_DENSE_CAPACITY : TWELL_OK;
+      }
+    }
+  }
+  __syncthreads();
+  const uint64_t mask = s_mask;
+  return ((mask >> n) & 1u) ? popc64(mask & ((uint64_t{1} << n) - 1u)) : -1;
+}
+
 // One workgroup per row.  A dense row is assembled in LDS (zeros, then the
 // stored slots scattered in), then written out 16 bytes per thread, taking the
 // overflowing tiles from the spill area; with `full_src` the row is copied
 // from h as is.  Finally the row's TwELL slots are cleared.
-template <typename E, bool IN_LDS>
+template <typename E, bool IN_LDS, bool ROUTE>
 __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
     int dff, int T, int C, int nt, const int32_t* __restrict__ row_map,
     const uint8_t* __restrict__ flags, const E* __restrict__ spill, const E* __restrict__ full_src,
     E* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
-    E* __restrict__ dense_values, int64_t cap) {
+    E* __restrict__ dense_values, int64_t cap, RouteOut ro) {
   constexpr int V = Vec16<E>::N;
   extern __shared__ __attribute__((aligned(16))) unsigned char mat_lds[];
   E* rowbuf = reinterpret_cast<E*>(mat_lds);
   const int64_t n = blockIdx.x;
-  const int m = row_map[n];
+  const int m = ROUTE ? route_rows_in_block(ro, flags, nt, cap, n) : row_map[n];
   if (m < 0) return;
   const int64_t slot0 = n * nt;
   const int nslots = nt * C;
@@ -248,12 +289,7 @@ __device__ __forceinline__ void load_slots(SlotGroup<CC, E>& g, const uint8_t* _
   }
 }
 
-// Rows routed by the scan (row_map), or, with ROUTE (at most 64 rows, one
-// workgroup per row), by the kernel itself: every workgroup ORs the tile
-// flags of all rows into LDS, one ballot over the rows gives each dense row
-// its index (dense rows below it, so ascending token order), and workgroup
-// 0 writes the dense-row list, the sparse-row list, their counts and the
-// status word, as the scan would.
+// Rows routed by the scan (row_map), or, with ROUTE, by route_rows_in_block.
 template <typename E, int CC, int NT, bool ROUTE>
 __global__ __launch_bounds__(NT) void materialize_slots_kernel(
     int dff, int T, int nt, const int32_t* __restrict__ row_map, const uint8_t* __restrict__ flags,
@@ -261,43 +297,7 @@ __global__ __launch_bounds__(NT) void materialize_slots_kernel(
     uint8_t* __restrict__ cnt, E* __restrict__ dense_values, int64_t cap, RouteOut ro) {
   constexpr int V = Vec16<E>::N, B = 4;
   const int64_t n = blockIdx.x;
-  int m;
-  if constexpr (ROUTE) {
-    static_assert(NT >= kWave, "one full wave for the row ballot");
-    __shared__ uint8_t s_rd[kWave];
-    __shared__ uint64_t s_mask;
-    const int N = static_cast<int>(ro.n_rows);  // at most 64
-    if (threadIdx.x < kWave) s_rd[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < N * nt; i += NT)
-      if (flags[i]) s_rd[i / nt] = 1;  // every writer stores 1
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      const int r = threadIdx.x;
-      const bool d = r < N && s_rd[r] != 0;
-      const uint64_t mask = wave_ballot(d);
-      if (r == 0) s_mask = mask;
-      if (n == 0 && r < N) {
-        const int below = popc_below(mask);  // dense rows below row r
-        if (d) {
-          if (below < cap) ro.dense_rows[below] = r;
-        } else {
-          ro.sparse_rows[r - below] = r;
-        }
-        if (r == 0) {
-          const int total = popc64(mask);
-          *ro.n_dense = total;
-          *ro.n_sparse = N - total;
-          if (ro.status != nullptr) *ro.status = total > cap ? TWELL_ERR_DENSE_CAPACITY : TWELL_OK;
-        }
-      }
-    }
-    __syncthreads();
-    const uint64_t mask = s_mask;
-    m = ((mask >> n) & 1u) ? popc64(mask & ((uint64_t{1} << n) - 1u)) : -1;
-  } else {
-    m = row_map[n];
-  }
+  const int m = ROUTE ? route_rows_in_block(ro, flags, nt, cap, n) : row_map[n];
   if (m < 0) return;
   const int64_t slot0 = n * nt;
   if (m < cap) {
@@ -423,9 +423,8 @@ hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* de
 }
 
 bool materialize_routes_itself(const Geometry& g, int elem_bytes, bool from_slots) {
-  const size_t row_bytes = static_cast<size_t>(g.d_ff) * elem_bytes;
-  return from_slots && g.n_rows > 0 && g.n_rows <= kSkinnyMaxRows &&
-         (g.capacity == 4 || g.capacity == 8) && row_bytes > 20 * 1024;
+  (void)elem_bytes;
+  return from_slots && g.n_rows > 0 && g.n_rows <= kSkinnyMaxRows;
 }
 
 hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const RouteBufs& rb,
@@ -480,27 +479,24 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   }
   const bool in_lds = full_src == nullptr && row_bytes <= 64 * 1024;
   const size_t lds = in_lds ? row_bytes : 0;
-  if (elem_bytes == 2 && in_lds) {
-    materialize_kernel<uint16_t, true><<<blocks, kRowThreads, lds, s>>>(
-        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
-        static_cast<const uint16_t*>(spill), static_cast<const uint16_t*>(full_src),
-        static_cast<uint16_t*>(vals), idx, cnt, static_cast<uint16_t*>(dense_values), dense_cap);
-  } else if (elem_bytes == 4 && in_lds) {
-    materialize_kernel<float, true><<<blocks, kRowThreads, lds, s>>>(
-        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags, static_cast<const float*>(spill),
-        static_cast<const float*>(full_src), static_cast<float*>(vals), idx, cnt,
-        static_cast<float*>(dense_values), dense_cap);
-  } else if (elem_bytes == 2) {
-    materialize_kernel<uint16_t, false><<<blocks, kRowThreads, lds, s>>>(
-        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
-        static_cast<const uint16_t*>(spill), static_cast<const uint16_t*>(full_src),
-        static_cast<uint16_t*>(vals), idx, cnt, static_cast<uint16_t*>(dense_values), dense_cap);
-  } else {
-    materialize_kernel<float, false><<<blocks, kRowThreads, lds, s>>>(
-        g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags, static_cast<const float*>(spill),
-        static_cast<const float*>(full_src), static_cast<float*>(vals), idx, cnt,
-        static_cast<float*>(dense_values), dense_cap);
-  }
+  const RouteOut ro = route != nullptr ? *route : RouteOut{};
+  auto go = [&](auto tag, auto lds_tag, auto route_tag) {
+    typedef decltype(tag) E;
+    materialize_kernel<E, decltype(lds_tag)::value, decltype(route_tag)::value>
+        <<<blocks, kRowThreads, lds, s>>>(g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
+                                          static_cast<const E*>(spill),
+                                          static_cast<const E*>(full_src), static_cast<E*>(vals),
+                                          idx, cnt, static_cast<E*>(dense_values), dense_cap, ro);
+  };
+  typedef std::integral_constant<bool, true> Yes;
+  typedef std::integral_constant<bool, false> No;
+  auto by_route = [&](auto tag, auto lds_tag) {
+    if (route != nullptr) go(tag, lds_tag, Yes{}); else go(tag, lds_tag, No{});
+  };
+  auto by_lds = [&](auto tag) {
+    if (in_lds) by_route(tag, Yes{}); else by_route(tag, No{});
+  };
+  if (elem_bytes == 2) by_lds(uint16_t{}); else by_lds(float{});
   return hipGetLastError();
 }
 

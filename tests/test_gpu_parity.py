@@ -279,13 +279,14 @@ def test_forward_bias_limits(dtype):
     assert_close_rel(as_f64(out.y), y_ref, TOL[cfg.torch_dtype])
 
 
-@pytest.mark.parametrize("n_rows,d_ff", [(200, 1024), (1500, 1024), (48, 12288)])
+@pytest.mark.parametrize("n_rows,d_ff", [(200, 1024), (1500, 1024), (60, 2048), (48, 12288)])
 def test_forward_dense_capacity_exceeded(n_rows, d_ff):
     """Too many dense rows: the status says so, n_dense is the true count and
     the first dense_capacity dense rows are stored, whether the capacity runs
     out early or at the last dense row, with the row flags ORed inside the
     scan (200 rows), by the separate row pass (1500 rows), or by the dense-row
-    build itself (48 rows of 24 KB)."""
+    build itself (at most 64 rows: rows of 4 KB built in LDS, of 24 KB from
+    slot groups)."""
     cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=128, d_ff=d_ff)
     t = make_inputs(cfg)
     total = run_forward(cfg, t).hybrid.n_dense_host()
