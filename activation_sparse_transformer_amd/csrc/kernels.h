@@ -88,7 +88,10 @@ hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* de
 // G2b: dense_values[m] = row n of h (from `full_src` if given, else from the
 // TwELL slots of the row plus the spilled overflowing tiles), then the row's
 // TwELL slots are cleared.
-// Routing outputs written by a dense-row build that routes the rows itself.
+// Routing outputs written by a dense-row build that routes the rows itself;
+// row_dense (one 0/1 byte per row) is given when the build counts the dense
+// rows below each row from it, and null when each workgroup ORs the tile flags
+// of all rows itself (at most 64 rows).
 struct RouteOut {
   int64_t n_rows;
   int32_t* dense_rows;
@@ -96,6 +99,7 @@ struct RouteOut {
   int32_t* sparse_rows;
   int32_t* n_sparse;
   int32_t* status;
+  const uint8_t* row_dense;
 };
 
 hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* row_map,
@@ -103,17 +107,19 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
                               void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
                               int64_t dense_cap, hipStream_t s, const RouteOut* route = nullptr);
 
-// G2a + G2b in one launch for batches of at most 64 rows: each row's
-// workgroup of the dense-row build ORs every row's tile flags itself and
-// numbers the dense rows with one ballot; writes what launch_route_scan and
-// launch_materialize write, except row_dense and row_map.
-// `materialize_routes_itself` says when it applies (from_slots: the rows come
-// from the forward's slots and spill, not from h).
-bool materialize_routes_itself(const Geometry& g, int elem_bytes, bool from_slots);
+// G2 without the scan kernel: route_mode says whether the dense-row build can
+// route the rows itself (1: at most 64 rows, each workgroup ORs every row's
+// tile flags and numbers the dense rows with one ballot; 2: more than 1024
+// and at most 16384 rows, row_or_kernel first, then each workgroup counts the
+// dense rows below its row from row_dense) or not (0).  Writes what
+// launch_route_scan and launch_materialize write, except row_map (and, in mode
+// 1, row_dense).  full_src: h when the rows are copied from it (twell_pack).
+int route_mode(const Geometry& g);
 hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const RouteBufs& rb,
-                                    const void* spill, void* vals, uint8_t* idx, uint8_t* cnt,
-                                    int32_t* dense_rows, void* dense_values, int64_t dense_cap,
-                                    int32_t* n_dense, int32_t* status, hipStream_t s);
+                                    const void* spill, const void* full_src, void* vals,
+                                    uint8_t* idx, uint8_t* cnt, int32_t* dense_rows,
+                                    void* dense_values, int64_t dense_cap, int32_t* n_dense,
+                                    int32_t* status, hipStream_t s);
 
 // G6: twell_to_dense.
 hipError_t launch_unpack(const Geometry& g, int elem_bytes, const void* vals, const uint8_t* idx,

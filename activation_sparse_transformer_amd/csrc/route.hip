@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kRowThreads = 256;
+constexpr int64_t kPrefixMaxRows = 16384;
 
 __device__ __forceinline__ bool row_has_flag(const uint8_t* __restrict__ f, int nt) {
   uint32_t any = 0;
@@ -187,11 +188,64 @@ __device__ int route_rows_in_block(const RouteOut& ro, const uint8_t* __restrict
   return ((mask >> n) & 1u) ? popc64(mask & ((uint64_t{1} << n) - 1u)) : -1;
 }
 
+// Routing once row_dense is known (row_or_kernel): workgroup n
+// counts the dense rows below row n itself (row_dense holds 0 or 1 per row, so
+// the popcount of each 16-byte piece counts them), writes its own entry of
+// the dense-row or the sparse-row list, and the last row's workgroup writes
+// the counts and the status word.  Returns the dense index of row n, or -1.
+__device__ int route_rows_prefix(const RouteOut& ro, int64_t cap, int64_t n) {
+  __shared__ int s_part[1024 / kWave];  // up to 1024 threads
+  const uint8_t* rd = ro.row_dense;
+  int c = 0;
+  for (int64_t i = static_cast<int64_t>(threadIdx.x) * 16; i < n;
+       i += static_cast<int64_t>(blockDim.x) * 16) {
+    if (i + 16 <= n) {
+      const uint4 v = *reinterpret_cast<const uint4*>(rd + i);
+      c += __popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w);
+    } else {
+      for (int64_t j = i; j < n; ++j) c += rd[j];
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) c += __shfl_xor(c, o, kWave);
+  if (lane_id() == 0) s_part[threadIdx.x / kWave] = c;
+  __syncthreads();
+  int below = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x) / kWave; ++w) below += s_part[w];
+  const int d = rd[n] != 0;
+  if (threadIdx.x == 0) {
+    if (d) {
+      if (below < cap) ro.dense_rows[below] = static_cast<int32_t>(n);
+    } else {
+      ro.sparse_rows[n - below] = static_cast<int32_t>(n);
+    }
+    if (n == ro.n_rows - 1) {
+      const int64_t total = static_cast<int64_t>(below) + d;
+      *ro.n_dense = static_cast<int32_t>(total);
+      *ro.n_sparse = static_cast<int32_t>(ro.n_rows - total);
+      if (ro.status != nullptr) *ro.status = total > cap ? TWELL_ERR_DENSE_CAPACITY : TWELL_OK;
+    }
+  }
+  return d ? below : -1;
+}
+
+// Dense index of row n: from the scan's row map (RM 0), routed inside the
+// workgroup (RM 1, at most 64 rows), or from the count of dense rows below
+// (RM 2).
+template <int RM>
+__device__ __forceinline__ int row_dense_index(const RouteOut& ro, const int32_t* row_map,
+                                               const uint8_t* flags, int nt, int64_t cap,
+                                               int64_t n) {
+  if constexpr (RM == 1) return route_rows_in_block(ro, flags, nt, cap, n);
+  else if constexpr (RM == 2) return route_rows_prefix(ro, cap, n);
+  else return row_map[n];
+}
+
 // One workgroup per row.  A dense row is assembled in LDS (zeros, then the
 // stored slots scattered in), then written out 16 bytes per thread, taking the
 // overflowing tiles from the spill area; with `full_src` the row is copied
 // from h as is.  Finally the row's TwELL slots are cleared.
-template <typename E, bool IN_LDS, bool ROUTE>
+template <typename E, bool IN_LDS, int RM>
 __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
     int dff, int T, int C, int nt, const int32_t* __restrict__ row_map,
     const uint8_t* __restrict__ flags, const E* __restrict__ spill, const E* __restrict__ full_src,
@@ -201,7 +255,7 @@ __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
   extern __shared__ __attribute__((aligned(16))) unsigned char mat_lds[];
   E* rowbuf = reinterpret_cast<E*>(mat_lds);
   const int64_t n = blockIdx.x;
-  const int m = ROUTE ? route_rows_in_block(ro, flags, nt, cap, n) : row_map[n];
+  const int m = row_dense_index<RM>(ro, row_map, flags, nt, cap, n);
   if (m < 0) return;
   const int64_t slot0 = n * nt;
   const int nslots = nt * C;
@@ -289,15 +343,15 @@ __device__ __forceinline__ void load_slots(SlotGroup<CC, E>& g, const uint8_t* _
   }
 }
 
-// Rows routed by the scan (row_map), or, with ROUTE, by route_rows_in_block.
-template <typename E, int CC, int NT, bool ROUTE>
+// Rows routed as row_dense_index says.
+template <typename E, int CC, int NT, int RM>
 __global__ __launch_bounds__(NT) void materialize_slots_kernel(
     int dff, int T, int nt, const int32_t* __restrict__ row_map, const uint8_t* __restrict__ flags,
     const E* __restrict__ spill, E* __restrict__ vals, uint8_t* __restrict__ idx,
     uint8_t* __restrict__ cnt, E* __restrict__ dense_values, int64_t cap, RouteOut ro) {
   constexpr int V = Vec16<E>::N, B = 4;
   const int64_t n = blockIdx.x;
-  const int m = ROUTE ? route_rows_in_block(ro, flags, nt, cap, n) : row_map[n];
+  const int m = row_dense_index<RM>(ro, row_map, flags, nt, cap, n);
   if (m < 0) return;
   const int64_t slot0 = n * nt;
   if (m < cap) {
@@ -422,18 +476,28 @@ hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* de
   return hipGetLastError();
 }
 
-bool materialize_routes_itself(const Geometry& g, int elem_bytes, bool from_slots) {
-  (void)elem_bytes;
-  return from_slots && g.n_rows > 0 && g.n_rows <= kSkinnyMaxRows;
+int route_mode(const Geometry& g) {
+  if (g.n_rows > 0 && g.n_rows <= kSkinnyMaxRows) return 1;
+  // above the scan's fused range the row pass runs anyway; each build
+  // workgroup then reads at most kPrefixMaxRows bytes of row flags
+  if (g.n_rows > kScanThreads && g.n_rows <= kPrefixMaxRows) return 2;
+  return 0;
 }
 
 hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const RouteBufs& rb,
-                                    const void* spill, void* vals, uint8_t* idx, uint8_t* cnt,
-                                    int32_t* dense_rows, void* dense_values, int64_t dense_cap,
-                                    int32_t* n_dense, int32_t* status, hipStream_t s) {
-  if (!materialize_routes_itself(g, elem_bytes, true)) return hipErrorInvalidValue;
-  const RouteOut ro{g.n_rows, dense_rows, n_dense, rb.sparse_rows, rb.n_sparse, status};
-  return launch_materialize(g, elem_bytes, nullptr, rb.flags, spill, nullptr, vals, idx, cnt,
+                                    const void* spill, const void* full_src, void* vals,
+                                    uint8_t* idx, uint8_t* cnt, int32_t* dense_rows,
+                                    void* dense_values, int64_t dense_cap, int32_t* n_dense,
+                                    int32_t* status, hipStream_t s) {
+  const int mode = route_mode(g);
+  if (mode == 0) return hipErrorInvalidValue;
+  if (mode == 2) {
+    const unsigned blocks = static_cast<unsigned>((g.n_rows + kRowThreads - 1) / kRowThreads);
+    row_or_kernel<<<blocks, kRowThreads, 0, s>>>(rb.flags, g.n_rows, g.n_tiles, rb.row_dense);
+  }
+  const RouteOut ro{g.n_rows, dense_rows, n_dense, rb.sparse_rows, rb.n_sparse, status,
+                    mode == 2 ? rb.row_dense : nullptr};
+  return launch_materialize(g, elem_bytes, nullptr, rb.flags, spill, full_src, vals, idx, cnt,
                             dense_values, dense_cap, s, &ro);
 }
 
@@ -442,6 +506,9 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
                               void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
                               int64_t dense_cap, hipStream_t s, const RouteOut* route) {
   if (g.n_rows == 0) return hipSuccess;
+  // 0: the scan's row map; 1: routed inside each workgroup; 2: counted from row_dense
+  const int rmode = route == nullptr ? 0 : route->row_dense == nullptr ? 1 : 2;
+  const RouteOut ro = route != nullptr ? *route : RouteOut{};
   const unsigned blocks = static_cast<unsigned>(g.n_rows);
   const size_t row_bytes = static_cast<size_t>(g.d_ff) * elem_bytes;
   // The LDS row buffer is the faster build while eight rows fit in a CU's
@@ -451,22 +518,23 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   if (full_src == nullptr && (g.capacity == 4 || g.capacity == 8) && row_bytes > 20 * 1024) {
     // A few rows (decode-sized batches) are latency-bound: 1024 threads per
     // row then rebuild a row in one batch of loads instead of several.
-    auto run = [&](auto tag, auto cc) {
+    auto run2 = [&](auto tag, auto cc, auto rm) {
       typedef decltype(tag) E;
-      if (g.n_rows <= kSkinnyMaxRows && route != nullptr)
-        materialize_slots_kernel<E, decltype(cc)::value, 1024, true><<<blocks, 1024, 0, s>>>(
-            g.d_ff, g.tile, g.n_tiles, nullptr, flags, static_cast<const E*>(spill),
-            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap, *route);
-      else if (g.n_rows <= kSkinnyMaxRows)
-        materialize_slots_kernel<E, decltype(cc)::value, 1024, false><<<blocks, 1024, 0, s>>>(
+      constexpr int RM = decltype(rm)::value;
+      if (g.n_rows <= kSkinnyMaxRows)
+        materialize_slots_kernel<E, decltype(cc)::value, 1024, RM><<<blocks, 1024, 0, s>>>(
             g.d_ff, g.tile, g.n_tiles, row_map, flags, static_cast<const E*>(spill),
-            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap, RouteOut{});
+            static_cast<E*>(vals), idx, cnt, static_cast<E*>(dense_values), dense_cap, ro);
       else
-        materialize_slots_kernel<E, decltype(cc)::value, kRowThreads, false>
+        materialize_slots_kernel<E, decltype(cc)::value, kRowThreads, RM>
             <<<blocks, kRowThreads, 0, s>>>(g.d_ff, g.tile, g.n_tiles, row_map, flags,
                                             static_cast<const E*>(spill), static_cast<E*>(vals),
-                                            idx, cnt, static_cast<E*>(dense_values), dense_cap,
-                                            RouteOut{});
+                                            idx, cnt, static_cast<E*>(dense_values), dense_cap, ro);
+    };
+    auto run = [&](auto tag, auto cc) {
+      if (rmode == 1) run2(tag, cc, std::integral_constant<int, 1>{});
+      else if (rmode == 2) run2(tag, cc, std::integral_constant<int, 2>{});
+      else run2(tag, cc, std::integral_constant<int, 0>{});
     };
     typedef std::integral_constant<int, 4> C4;
     typedef std::integral_constant<int, 8> C8;
@@ -479,7 +547,6 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   }
   const bool in_lds = full_src == nullptr && row_bytes <= 64 * 1024;
   const size_t lds = in_lds ? row_bytes : 0;
-  const RouteOut ro = route != nullptr ? *route : RouteOut{};
   auto go = [&](auto tag, auto lds_tag, auto route_tag) {
     typedef decltype(tag) E;
     materialize_kernel<E, decltype(lds_tag)::value, decltype(route_tag)::value>
@@ -491,7 +558,9 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   typedef std::integral_constant<bool, true> Yes;
   typedef std::integral_constant<bool, false> No;
   auto by_route = [&](auto tag, auto lds_tag) {
-    if (route != nullptr) go(tag, lds_tag, Yes{}); else go(tag, lds_tag, No{});
+    if (rmode == 1) go(tag, lds_tag, std::integral_constant<int, 1>{});
+    else if (rmode == 2) go(tag, lds_tag, std::integral_constant<int, 2>{});
+    else go(tag, lds_tag, std::integral_constant<int, 0>{});
   };
   auto by_lds = [&](auto tag) {
     if (in_lds) by_route(tag, Yes{}); else by_route(tag, No{});

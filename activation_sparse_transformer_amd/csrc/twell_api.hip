@@ -147,10 +147,10 @@ AuxStream* aux_stream(hipError_t* err) {
 // the dense rows, sparse product, dense fallback.
 int route_and_materialize(const Geometry& g, int eb, const PackWorkspace& w, const void* full_src,
                           const twell_hybrid* hy, int32_t* d_status, hipStream_t st) {
-  if (materialize_routes_itself(g, eb, full_src == nullptr)) {
-    // few rows: the dense-row build routes them itself (one launch instead of two)
-    TWELL_TRY(launch_route_materialize(g, eb, w.route, w.spill, hy->values, hy->indices,
-                                       hy->counts, hy->dense_rows, hy->dense_values,
+  if (route_mode(g) != 0) {
+    // the dense-row build routes the rows itself: no scan kernel
+    TWELL_TRY(launch_route_materialize(g, eb, w.route, w.spill, full_src, hy->values,
+                                       hy->indices, hy->counts, hy->dense_rows, hy->dense_values,
                                        hy->dense_capacity, hy->n_dense, d_status, st));
     return TWELL_OK;
   }
