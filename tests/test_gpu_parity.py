@@ -157,6 +157,26 @@ def test_spmm_many_rows_integer_exact(n, dm, dff, T, density):
     np.testing.assert_array_equal(as_f64(y), y_ref)
 
 
+def test_spmm_large_fallback_tiles_integer_exact():
+    """Enough rows and columns for the fallback's 256 x 256 tiles (at least
+    2048 of them in the worst case): about half of 8000 rows dense, every
+    value of y checked, all products and sums exact in bf16."""
+    n, dm, T = 8000, 16384, 128
+    say(f"spmm large fallback tiles n={n} dm={dm}")
+    rng = np.random.default_rng(8000)
+    h = rng.integers(-2, 3, size=(n, T)).astype(np.float32)
+    h[rng.random((n, T)) >= 0.013] = 0
+    w = rng.integers(-1, 2, size=(T, dm)).astype(np.float32)
+    hy, _ = twell.twell_pack(torch.from_numpy(h).to(torch.bfloat16).cuda(), T, 1)
+    y = twell.twell_spmm(hy, torch.from_numpy(w).to(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    ref_h = assert_pack_matches(hy, h)
+    assert n // 4 < ref_h.n_dense < 3 * n // 4
+    y_ref = (oracle.unpack(ref_h) @ w).astype(np.float32)  # integers below 2^8: exact
+    assert np.max(np.abs(y_ref)) <= 256
+    np.testing.assert_array_equal(as_f32(y), y_ref)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_spmm_identity_is_unpack(dtype):
     ht, hh = sparse_h(9, 90, 256, 0.05, DT[dtype])
