@@ -46,7 +46,7 @@ CALIB_COPY_BYTES = 256 << 20
 # kernels each stage launches for bf16 layers with d_model a multiple of 512
 STAGE_KERNELS = {
     "up_gemm_pack": "up_pack_bf16_fast",
-    "route": "row_or_kernel + route_scan_kernel + materialize_kernel",
+    "route": "row_or_kernel + materialize_kernel",
     "spmm_sparse": "spmm_list_bf16_kernel",
     "fallback_gemm": "fallback_bf16_fast",
 }
