@@ -49,11 +49,16 @@ def test_pack_unpack_bitexact(dtype, T, C, density, n):
     np.testing.assert_array_equal(u32(as_f32(u)), u32(oracle.unpack(ref)))
 
 
-@pytest.mark.parametrize("n,dff,T,density", [(1024, 1024, 64, 0.02), (1000, 192, 64, 0.06),
-                                             (1025, 1024, 64, 0.02), (2500, 200 * 64, 64, 0.01)])
+@pytest.mark.parametrize("n,dff,T,density", [(64, 1024, 64, 0.03), (65, 1024, 64, 0.03),
+                                             (1024, 1024, 64, 0.02), (1000, 192, 64, 0.06),
+                                             (1025, 1024, 64, 0.02), (2500, 200 * 64, 64, 0.01),
+                                             (16384, 512, 128, 0.01), (16385, 512, 128, 0.01)])
 def test_pack_routing_row_counts(n, dff, T, density):
-    """Row routing with the row flags ORed inside the scan (up to 1024 rows)
-    and by the separate row pass beyond, tile counts a multiple of 16 or not."""
+    """Row routing on both sides of every switch: inside the dense-row build's
+    workgroups (up to 64 rows), the scan with the row flags ORed inside it (up
+    to 1024), the build counting dense rows below each row after the row pass
+    (up to 16384), the row pass and the scan beyond; tile counts a multiple
+    of 16 or not."""
     say(f"pack routing n={n} dff={dff} T={T}")
     ht, hh = sparse_h(77 + n, n, dff, density, torch.bfloat16)
     hy, status = twell.twell_pack(ht.cuda(), T, 4)
@@ -235,6 +240,8 @@ SMALL = [
     ("large_bf16", 33, 64, 10752),
     ("ffn_1b_bf16", 64, 192, 10368),
     ("decode_bf16", 1, 128, 12288),
+    # 65 rows: past the split-K kernels and the in-workgroup routing
+    ("ffn_1b_bf16", 65, 192, 2048),
 ]
 
 
