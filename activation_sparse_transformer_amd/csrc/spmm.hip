@@ -12,6 +12,8 @@
 // 64 at a time (coalesced), ballots the live ones, and walks them with
 // readlane so the row index and value are wave-uniform scalars; each live
 // slot then costs one coalesced 16-byte load of w_down per lane.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -201,7 +203,86 @@ __device__ __forceinline__ void dot2_row(float (&acc)[VEC], uint32_t vlo, uint32
 // time with broadcast LDS reads, keeping 8 row gathers in flight.
 constexpr int kListUnroll = 8;
 
-template <int VEC>
+// The row's live slots into the wave's LDS list in ascending slot order
+// (byte offset of the w_down row, value); returns their number.  SPL > 0: the
+// row has exactly 64 * SPL slots and lane l takes slots [l * SPL, l * SPL +
+// SPL), all loaded in one round (one index load and one value load of SPL
+// elements when SPL is 4 or 8), and a 4-ballot prefix sum of the lanes' live
+// counts places them; SPL == 0: 64 slots per round for any slot count.
+template <int SPL>
+__device__ __forceinline__ int compact_row(const uint16_t* __restrict__ vals,
+                                           const uint8_t* __restrict__ idx,
+                                           const uint8_t* __restrict__ cnt, int64_t n, int nt,
+                                           int C, int T, int dm, int nslots, uint2* list) {
+  const int lane = lane_id();
+  const int64_t s0 = n * nslots;
+  if constexpr (SPL > 0) {
+    uint8_t li[SPL];
+    uint16_t lv[SPL];
+    uint8_t lc[SPL];
+    const int sb = lane * SPL;
+    if constexpr (SPL == 4) {
+      *reinterpret_cast<uint32_t*>(li) = *reinterpret_cast<const uint32_t*>(idx + s0 + sb);
+      *reinterpret_cast<uint2*>(lv) = *reinterpret_cast<const uint2*>(vals + s0 + sb);
+    } else if constexpr (SPL == 8) {
+      *reinterpret_cast<uint2*>(li) = *reinterpret_cast<const uint2*>(idx + s0 + sb);
+      *reinterpret_cast<uint4*>(lv) = *reinterpret_cast<const uint4*>(vals + s0 + sb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) li[i] = idx[s0 + sb + i], lv[i] = vals[s0 + sb + i];
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) lc[i] = cnt[n * nt + (sb + i) / C];
+    bool live[SPL];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int s = sb + i;
+      live[i] = (s - (s / C) * C) < static_cast<int>(lc[i]) && static_cast<int>(li[i]) < T;
+      mine += live[i];
+    }
+    int before = 0, total = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {  // mine <= SPL <= 8
+      const uint64_t m = wave_ballot((mine >> b) & 1);
+      before += popc_below(m) << b;
+      total += popc64(m) << b;
+    }
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      if (live[i]) {
+        const int s = sb + i;
+        const int t = s / C;
+        list[before++] = make_uint2(
+            static_cast<uint32_t>(t * T + li[i]) * static_cast<uint32_t>(dm) * 2u, lv[i]);
+      }
+    }
+    return total;
+  } else {
+    int nnz = 0;
+    for (int g = 0; g < nslots; g += kWave) {
+      const int s = g + lane;
+      bool live = false;
+      uint32_t off = 0, v = 0;
+      if (s < nslots) {
+        const int t = s / C;
+        const int k = s - t * C;
+        if (k < static_cast<int>(cnt[n * nt + t])) {
+          const int local = static_cast<int>(idx[s0 + s]);
+          live = local < T;  // a malformed index is ignored rather than read out of bounds
+          off = static_cast<uint32_t>(t * T + local) * static_cast<uint32_t>(dm) * 2u;
+          v = vals[s0 + s];
+        }
+      }
+      const uint64_t m = wave_ballot(live);
+      if (live) list[nnz + popc_below(m)] = make_uint2(off, v);
+      nnz += popc64(m);
+    }
+    return nnz;
+  }
+}
+
+template <int VEC, int SPL>
 __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
     const uint16_t* __restrict__ vals, const uint8_t* __restrict__ idx,
     const uint8_t* __restrict__ cnt, const int32_t* __restrict__ rows,
@@ -222,26 +303,7 @@ __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
   const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
   for (int64_t k = part + parts * wid; k < R; k += parts * per_xcd_waves) {
     const int64_t n = rows != nullptr ? rows[k] : k;
-    const int64_t s0 = n * nslots;
-    int nnz = 0;
-    for (int g = 0; g < nslots; g += kWave) {
-      const int s = g + lane;
-      bool live = false;
-      uint32_t off = 0, v = 0;
-      if (s < nslots) {
-        const int t = s / C;
-        const int k = s - t * C;
-        if (k < static_cast<int>(cnt[n * nt + t])) {
-          const int local = static_cast<int>(idx[s0 + s]);
-          live = local < T;  // a malformed index is ignored rather than read out of bounds
-          off = static_cast<uint32_t>(t * T + local) * static_cast<uint32_t>(dm) * 2u;
-          v = vals[s0 + s];
-        }
-      }
-      const uint64_t m = wave_ballot(live);
-      if (live) list[nnz + popc_below(m)] = make_uint2(off, v);
-      nnz += popc64(m);
-    }
+    const int nnz = compact_row<SPL>(vals, idx, cnt, n, nt, C, T, dm, nslots, list);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's list is in LDS
     float acc[VEC];
 #pragma unroll
@@ -479,14 +541,23 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
               g.n_tiles, n_slices, tpw);
         return hipGetLastError();
       }
-      if (vec == 8)
-        spmm_list_bf16_kernel<8><<<xblocks, kThreads, list_bytes, s>>>(
-            v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
-            n_slices);
-      else
-        spmm_list_bf16_kernel<16><<<xblocks, kThreads, list_bytes, s>>>(
-            v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles,
-            n_slices);
+      // slots per lane when a row's slots fill whole waves (4 at the 1B layer)
+      const int nslots = g.n_tiles * g.capacity;
+      const int spl = nslots % kWave == 0 ? nslots / kWave : 0;
+      auto go = [&](auto vc, auto sc) {
+        spmm_list_bf16_kernel<decltype(vc)::value, decltype(sc)::value>
+            <<<xblocks, kThreads, list_bytes, s>>>(v16, idx, cnt, rows, n_rows_dev, w16, y16,
+                                                   g.n_rows, g.d_model, g.tile, g.capacity,
+                                                   g.n_tiles, n_slices);
+      };
+      auto by_spl = [&](auto vc) {
+        if (spl == 2) go(vc, std::integral_constant<int, 2>{});
+        else if (spl == 4) go(vc, std::integral_constant<int, 4>{});
+        else if (spl == 8) go(vc, std::integral_constant<int, 8>{});
+        else go(vc, std::integral_constant<int, 0>{});
+      };
+      if (vec == 8) by_spl(std::integral_constant<int, 8>{});
+      else by_spl(std::integral_constant<int, 16>{});
       return hipGetLastError();
     }
     {  // few rows, d_model the sliced kernel does not take: split each row over 16 waves

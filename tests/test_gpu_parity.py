@@ -162,6 +162,28 @@ def test_spmm_many_rows_integer_exact(n, dm, dff, T, density):
     np.testing.assert_array_equal(as_f64(y), y_ref)
 
 
+@pytest.mark.parametrize("n,dm,dff,C", [(1500, 512, 4096, 4), (1500, 1024, 8192, 4),
+                                         (1300, 512, 8192, 8)])
+def test_spmm_whole_wave_rows_integer_exact(n, dm, dff, C):
+    """Rows whose slots fill whole waves (2, 4 or 8 slots per lane): each lane
+    loads its slots in one round; every value of y checked, exact."""
+    T = 128
+    say(f"spmm whole-wave rows n={n} dm={dm} dff={dff} C={C}")
+    rng = np.random.default_rng(n + dff + C)
+    h = rng.integers(-2, 3, size=(n, dff)).astype(np.float32)
+    h[rng.random((n, dff)) >= (0.01 if C == 4 else 0.03)] = 0
+    w = rng.integers(-1, 2, size=(dff, dm)).astype(np.float32)
+    w[rng.random((dff, dm)) < 0.7] = 0
+    hy, _ = twell.twell_pack(torch.from_numpy(h).to(torch.bfloat16).cuda(), T, C)
+    y = twell.twell_spmm(hy, torch.from_numpy(w).to(torch.bfloat16).cuda())
+    torch.cuda.synchronize()
+    ref_h = assert_pack_matches(hy, h)
+    assert 0 < ref_h.n_dense < n
+    y_ref = oracle.spmm(ref_h, w.astype(np.float64))
+    assert np.max(np.abs(y_ref)) <= 256
+    np.testing.assert_array_equal(as_f64(y), y_ref)
+
+
 def test_spmm_large_fallback_tiles_integer_exact():
     """Enough rows and columns for the fallback's 256 x 256 tiles (at least
     2048 of them in the worst case): about half of 8000 rows dense, every
