@@ -142,12 +142,13 @@ size_t ffn_sparse_workspace_size(const twell_shape* shape);
  *      of value * w_down[t*tile + index];
  *   4. dense fallback GEMM for the dense rows: y[dense_rows[m]] =
  *      dense_values[m] W_down.
- * Steps 3 and 4 write disjoint rows of y and run concurrently: step 3 on a
- * library-owned auxiliary stream of the current device (created on the first
- * call, kept until the process ends), forked from and joined back into
- * `stream` with events, so all work still completes in `stream` order and the
- * pass can be captured into a HIP graph from `stream`.  Calls on one device
- * share that auxiliary stream.
+ * Steps 3 and 4 write disjoint rows of y.  For more than 64 rows they run
+ * concurrently: step 3 on a library-owned auxiliary stream of the current
+ * device (created on the first such call, kept until the process ends),
+ * forked from and joined back into `stream` with events, so all work still
+ * completes in `stream` order and the pass can be captured into a HIP graph
+ * from `stream`.  Calls on one device share that auxiliary stream.  For at
+ * most 64 rows both run in order on `stream`.
  * Arguments: shape (host pointer); x, w_up_t, b_up, w_down inputs; y output;
  * h_out (host pointer to a struct of device pointers) receives h in hybrid
  * TwELL form; h_dense_debug, if non-NULL, receives h [n_rows][d_ff] exactly
