@@ -19,6 +19,7 @@
 // staging, so both operands are read from LDS the same way.
 #include "common.h"
 #include "kernels.h"
+#include "spmm_split.h"
 
 namespace twell {
 namespace {
@@ -859,14 +860,15 @@ __global__ __launch_bounds__(CF::NT) void skinny_up_partial_bf16(
     }
 }
 
+// One (column block, K slice) of the fallback's split-K partial sums.
 template <class CF>
-__global__ __launch_bounds__(CF::NT) void skinny_fallback_partial_bf16(
+__device__ __forceinline__ void skinny_fallback_partial_tile(
     const uint16_t* __restrict__ dense_values, const int32_t* __restrict__ n_dense, int m_cap,
-    const uint16_t* __restrict__ w_down, int N, int K, int kw, int mm, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+    const uint16_t* __restrict__ w_down, int N, int K, int kw, int mm, float* __restrict__ part,
+    int nblk, int slice, uint16_t* lds) {
   const int M = min(*n_dense, m_cap);
   if (M <= 0) return;
-  const int n0 = blockIdx.x * CF::BN, slice = blockIdx.y, kbeg = slice * kw;
+  const int n0 = nblk * CF::BN, kbeg = slice * kw;
   f32x4_t acc[CF::FM][CF::FN];
   fast::mainloop_kn<CF>(dense_values + kbeg, K, M, 0, w_down + static_cast<int64_t>(kbeg) * N, N,
                         N, n0, min(kw, K - kbeg), lds, acc);
@@ -885,6 +887,45 @@ __global__ __launch_bounds__(CF::NT) void skinny_fallback_partial_bf16(
         if (col < N) dst[static_cast<int64_t>(m) * N + col] = acc[i][j][r];
       }
     }
+}
+
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void skinny_fallback_partial_bf16(
+    const uint16_t* __restrict__ dense_values, const int32_t* __restrict__ n_dense, int m_cap,
+    const uint16_t* __restrict__ w_down, int N, int K, int kw, int mm, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+  skinny_fallback_partial_tile<CF>(dense_values, n_dense, m_cap, w_down, N, K, kw, mm, part,
+                                   blockIdx.x, blockIdx.y, lds);
+}
+
+// The few-row sparse product of the TwELL rows in workgroups [0, sp_blocks)
+// (one per (row, XCD column slice); sp_blocks is a multiple of 8, so the XCD
+// is the workgroup index mod 8 as in its own kernel), and the fallback's
+// split-K partial sums in the workgroups after them.  The two write disjoint
+// memory (y of the sparse rows, partial sums), so the sparse gathers run
+// inside the fallback's weight stream instead of after it; the sparse
+// workgroups come first so they start at once.  Each of the CF::NW waves
+// takes 16 / CF::NW of the row's 16 tile ranges in turn, so the row's sum is
+// the same bits as with the 16-wave kernel.
+
+template <class CF, int VEC>
+__global__ __launch_bounds__(CF::NT) void skinny_fallback_partial_spmm_bf16(
+    const uint16_t* __restrict__ dense_values, const int32_t* __restrict__ n_dense, int m_cap,
+    const uint16_t* __restrict__ w_down, int N, int K, int kw, int mm, float* __restrict__ part,
+    int nb, int sp_blocks, SpmmRows sr, uint16_t* __restrict__ y, int64_t rows_max, int T, int C,
+    int nt, int n_slices, int tpw) {
+  static_assert(kSplitParts % CF::NW == 0, "whole tile ranges per wave");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+  const int b = blockIdx.x;
+  if (b < sp_blocks) {
+    spmm_split_rows<VEC, CF::NW, kSplitParts / CF::NW>(
+        sr.vals, sr.idx, sr.cnt, sr.rows, sr.n_rows, w_down, y, rows_max, N, T, C, nt, n_slices,
+        tpw, reinterpret_cast<uint2*>(lds), b, sp_blocks);
+    return;
+  }
+  const int f = b - sp_blocks;
+  skinny_fallback_partial_tile<CF>(dense_values, n_dense, m_cap, w_down, N, K, kw, mm, part,
+                                   f % nb, f / nb, lds);
 }
 
 // 32 rows x 128 columns (4 waves side by side) or 64 x 128 (2 x 2 waves):
@@ -921,6 +962,29 @@ hipError_t skinny_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
       dense_values, n_dense, m_cap, w_down, N, K, sp.kw, sp.mm, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_skinny_fallback_reduce<uint16_t>(g, sp, part, n_dense, m_cap, dense_rows, y, s);
+}
+
+template <class CF>
+hipError_t skinny_fallback_spmm_bf16(const Geometry& g, const uint16_t* dense_values,
+                                     const int32_t* dense_rows, const int32_t* n_dense, int m_cap,
+                                     const uint16_t* w_down, uint16_t* y, float* part,
+                                     const SpmmRows& sr, const SpmmSplitPlan& pl, hipStream_t s) {
+  const int N = g.d_model, K = g.d_ff;
+  const int nb = (N + CF::BN - 1) / CF::BN;
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb, fast::BKF, kSkinnyTargetBlocks);
+  const unsigned grid = pl.blocks + static_cast<unsigned>(nb * sp.slices);
+  const int sp_blocks = static_cast<int>(pl.blocks);  // 8 x rows per XCD
+  if (pl.vec == 8)
+    skinny_fallback_partial_spmm_bf16<CF, 8><<<grid, CF::NT, 0, s>>>(
+        dense_values, n_dense, m_cap, w_down, N, K, sp.kw, sp.mm, part, nb, sp_blocks, sr, y,
+        g.n_rows, g.tile, g.capacity, g.n_tiles, pl.n_slices, pl.tpw);
+  else
+    skinny_fallback_partial_spmm_bf16<CF, 16><<<grid, CF::NT, 0, s>>>(
+        dense_values, n_dense, m_cap, w_down, N, K, sp.kw, sp.mm, part, nb, sp_blocks, sr, y,
+        g.n_rows, g.tile, g.capacity, g.n_tiles, pl.n_slices, pl.tpw);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || m_cap == 0) return e;  // no dense row can be stored: nothing to sum
   return launch_skinny_fallback_reduce<uint16_t>(g, sp, part, n_dense, m_cap, dense_rows, y, s);
 }
 
@@ -1000,6 +1064,33 @@ hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
         dense_values, dense_rows, n_dense, dense_cap, w_down, y, g.n_rows, N, K);
   }
   return hipGetLastError();
+}
+
+bool fallback_takes_spmm(const Geometry& g) {
+  if (g.n_rows <= 0 || g.n_rows > kSkinnyMaxRows || g.d_ff % 64 != 0) return false;
+  SpmmSplitPlan pl;
+  if (!spmm_split_plan(g, 4, kSplitParts / 4, &pl)) return false;
+  static_assert(SkinnyCfg32::NW == 4 && SkinnyCfg64::NW == 4, "4 sparse waves per workgroup");
+  const size_t lds = 2 * static_cast<size_t>(g.n_rows <= 32 ? SkinnyCfg32::STAGE
+                                                             : SkinnyCfg64::STAGE) * 2;
+  return pl.lds_bytes <= lds;
+}
+
+hipError_t launch_fallback_bf16_with_spmm(const Geometry& g, const uint16_t* dense_values,
+                                          const int32_t* dense_rows, const int32_t* n_dense,
+                                          int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
+                                          hipStream_t s, float* skinny, const SpmmRows& sr) {
+  SpmmSplitPlan pl;
+  if (skinny == nullptr || !fallback_takes_spmm(g) || !spmm_split_plan(g, 4, kSplitParts / 4, &pl))
+    return hipErrorInvalidValue;
+  const int64_t worst = dense_cap < g.n_rows ? dense_cap : g.n_rows;
+  const int m_cap = static_cast<int>(worst > 0 ? worst : 0);
+  return g.n_rows <= 32 ? skinny_fallback_spmm_bf16<SkinnyCfg32>(g, dense_values, dense_rows,
+                                                                  n_dense, m_cap, w_down, y,
+                                                                  skinny, sr, pl, s)
+                        : skinny_fallback_spmm_bf16<SkinnyCfg64>(g, dense_values, dense_rows,
+                                                                  n_dense, m_cap, w_down, y,
+                                                                  skinny, sr, pl, s);
 }
 
 }  // namespace twell

@@ -139,6 +139,37 @@ hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
                                 const int32_t* dense_rows, const int32_t* n_dense,
                                 int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
                                 hipStream_t s, float* skinny = nullptr);
+
+// The few-row sparse product's launch plan for workgroups of `waves` waves,
+// each taking `parts_per_wave` of the row's waves * parts_per_wave tile
+// ranges: column slices, columns per lane, tiles per range, workgroups, LDS
+// bytes.  False when launch_spmm_sparse would not take that kernel.
+struct SpmmSplitPlan {
+  int n_slices, vec, tpw;
+  unsigned blocks;
+  size_t lds_bytes;
+};
+bool spmm_split_plan(const Geometry& g, int waves, int parts_per_wave, SpmmSplitPlan* plan);
+
+// The TwELL rows the sparse product reads (bf16 values).
+struct SpmmRows {
+  const uint16_t* vals;
+  const uint8_t* idx;
+  const uint8_t* cnt;
+  const int32_t* rows;    // the sparse rows, ascending
+  const int32_t* n_rows;  // device count of rows
+};
+
+// Batches of at most 64 rows (bf16): whether launch_fallback_bf16_with_spmm
+// can run the sparse product inside the fallback's split-K partial-sum launch
+// (extra workgroups of the same size, their slot lists in its LDS), and that
+// launch: y of the sparse rows, then the fallback's slice sums for the dense
+// rows, as launch_spmm_sparse followed by launch_fallback_bf16.
+bool fallback_takes_spmm(const Geometry& g);
+hipError_t launch_fallback_bf16_with_spmm(const Geometry& g, const uint16_t* dense_values,
+                                          const int32_t* dense_rows, const int32_t* n_dense,
+                                          int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
+                                          hipStream_t s, float* skinny, const SpmmRows& sr);
 hipError_t launch_fallback_f32(const Geometry& g, const float* dense_values,
                                const int32_t* dense_rows, const int32_t* n_dense,
                                int64_t dense_cap, const float* w_down, float* y, hipStream_t s,

@@ -16,6 +16,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "spmm_split.h"
 
 namespace twell {
 namespace {
@@ -153,55 +154,6 @@ __global__ __launch_bounds__(kThreads) void spmm_sparse_kernel(
 // takes one row at a time over its slice: VEC consecutive columns per lane.
 // bf16 products use v_dot2_f32_bf16 with one half of the value operand zero:
 // y[c] += v*W[c] as a single exact-product, single-rounding step per element.
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-
-template <int VEC>
-struct WVec;
-template <>
-struct WVec<4> {
-  uint32_t d[2];
-};
-template <>
-struct WVec<8> {
-  uint32_t d[4];
-};
-template <>
-struct WVec<16> {
-  uint32_t d[8];
-};
-
-template <int VEC>
-__device__ __forceinline__ void load_wvec(WVec<VEC>& o, const uint16_t* p) {
-  if constexpr (VEC == 4) {
-    const uint2 q = *reinterpret_cast<const uint2*>(p);
-    o.d[0] = q.x, o.d[1] = q.y;
-  } else {
-#pragma unroll
-    for (int h = 0; h < VEC / 8; ++h) {
-      const uint4 q = *reinterpret_cast<const uint4*>(p + 8 * h);
-      o.d[4 * h] = q.x, o.d[4 * h + 1] = q.y, o.d[4 * h + 2] = q.z, o.d[4 * h + 3] = q.w;
-    }
-  }
-}
-
-template <int VEC>
-__device__ __forceinline__ void dot2_row(float (&acc)[VEC], uint32_t vlo, uint32_t vhi,
-                                         const WVec<VEC>& w) {
-  const bf16x2_t a0 = __builtin_bit_cast(bf16x2_t, vlo);  // (v, 0)
-  const bf16x2_t a1 = __builtin_bit_cast(bf16x2_t, vhi);  // (0, v)
-#pragma unroll
-  for (int i = 0; i < VEC / 2; ++i) {
-    const bf16x2_t b = __builtin_bit_cast(bf16x2_t, w.d[i]);
-    acc[2 * i] = __builtin_amdgcn_fdot2_f32_bf16(a0, b, acc[2 * i], false);
-    acc[2 * i + 1] = __builtin_amdgcn_fdot2_f32_bf16(a1, b, acc[2 * i + 1], false);
-  }
-}
-
-// Each wave takes one row of its XCD's column slice at a time: it first
-// compacts the row's live slots into a per-wave LDS list (byte offset of the
-// w_down row, value) with a ballot prefix, then walks the list 8 entries at a
-// time with broadcast LDS reads, keeping 8 row gathers in flight.
-constexpr int kListUnroll = 8;
 
 // The row's live slots into the wave's LDS list in ascending slot order
 // (byte offset of the w_down row, value); returns their number.  SPL > 0: the
@@ -348,71 +300,8 @@ __global__ __launch_bounds__(P * kWave) void spmm_split_bf16_kernel(
     const int32_t* __restrict__ n_rows_dev, const uint16_t* __restrict__ w,
     uint16_t* __restrict__ y, int64_t N, int dm, int T, int C, int nt, int n_slices, int tpw) {
   extern __shared__ uint2 spmm_lists[];
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int wslots = tpw * C;
-  uint2* list = spmm_lists + wave * wslots;
-  float* red = reinterpret_cast<float*>(spmm_lists + P * wslots);  // [P][VEC][64]
-  const int xcd = blockIdx.x % 8;
-  const int slice = xcd % n_slices;
-  const int parts = 8 / n_slices;
-  const int part = xcd / n_slices;
-  const int64_t per_xcd = gridDim.x / 8;
-  const int col = slice * (kWave * VEC) + lane * VEC;
-  const char* wbase = reinterpret_cast<const char*>(w + col);
-  const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
-  const int t0 = wave * tpw, t1 = min(nt, t0 + tpw);
-  for (int64_t k = part + parts * static_cast<int64_t>(blockIdx.x / 8); k < R;
-       k += parts * per_xcd) {
-    const int64_t n = rows != nullptr ? rows[k] : k;
-    const int64_t s0 = n * nt * C;
-    int nnz = 0;
-    for (int g = t0 * C; g < t1 * C; g += kWave) {
-      const int s = g + lane;
-      bool live = false;
-      uint32_t off = 0, v = 0;
-      if (s < t1 * C) {
-        const int t = s / C;
-        const int kk = s - t * C;
-        if (kk < static_cast<int>(cnt[n * nt + t])) {
-          const int local = static_cast<int>(idx[s0 + s]);
-          live = local < T;  // a malformed index is ignored rather than read out of bounds
-          off = static_cast<uint32_t>(t * T + local) * static_cast<uint32_t>(dm) * 2u;
-          v = vals[s0 + s];
-        }
-      }
-      const uint64_t m = wave_ballot(live);
-      if (live) list[nnz + popc_below(m)] = make_uint2(off, v);
-      nnz += popc64(m);
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's list is in LDS
-    float acc[VEC];
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-    for (int q = 0; q < nnz; q += kListUnroll) {
-      uint2 e[kListUnroll];
-      WVec<VEC> wv[kListUnroll];
-#pragma unroll
-      for (int u = 0; u < kListUnroll; ++u) {
-        e[u] = list[min(q + u, nnz - 1)];  // past the end: reread the last entry, unused
-        load_wvec<VEC>(wv[u], reinterpret_cast<const uint16_t*>(wbase + e[u].x));
-      }
-#pragma unroll
-      for (int u = 0; u < kListUnroll; ++u)
-        if (q + u < nnz) dot2_row<VEC>(acc, e[u].y, e[u].y << 16, wv[u]);
-    }
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) red[(wave * VEC + i) * kWave + lane] = acc[i];
-    __syncthreads();
-    // wave w finishes columns i = w, w + P, ... of each lane's VEC
-    uint16_t* dst = y + n * dm + col;
-    for (int i = wave; i < VEC; i += P) {
-      float sum = 0.f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) sum += red[(p * VEC + i) * kWave + lane];
-      dst[i] = ElemTraits<uint16_t>::from_f32(sum);
-    }
-    __syncthreads();  // red and the lists are reused by the next row
-  }
+  spmm_split_rows<VEC, P>(vals, idx, cnt, rows, n_rows_dev, w, y, N, dm, T, C, nt, n_slices, tpw,
+                          spmm_lists, blockIdx.x, gridDim.x);
 }
 
 // Few rows, float32 (or a d_model the XCD-sliced kernel does not take): one
@@ -492,6 +381,27 @@ __global__ __launch_bounds__(P * kWave) void spmm_split_kernel(
 
 }  // namespace
 
+bool spmm_split_plan(const Geometry& g, int waves, int parts_per_wave, SpmmSplitPlan* plan) {
+  // the conditions under which launch_spmm_sparse takes spmm_split_bf16_kernel
+  if (g.n_rows <= 0 || g.d_model % 512 != 0) return false;
+  const int ns = g.d_model / 512;
+  int n_slices = 0, vec = 0;
+  if (ns == 1 || ns == 2 || ns == 4 || ns == 8) n_slices = ns, vec = 8;
+  else if (ns == 16) n_slices = 8, vec = 16;
+  if (n_slices == 0) return false;
+  const size_t list_bytes = static_cast<size_t>(kWavesPerBlock) * g.n_tiles * g.capacity * 8;
+  const bool offsets_fit = static_cast<int64_t>(g.d_ff) * g.d_model * 2 < (int64_t{1} << 32);
+  if (list_bytes > 64 * 1024 || !offsets_fit || g.n_rows * n_slices > 1024) return false;
+  const int tpw = (g.n_tiles + waves * parts_per_wave - 1) / (waves * parts_per_wave);
+  plan->n_slices = n_slices;
+  plan->vec = vec;
+  plan->tpw = tpw;
+  plan->blocks = static_cast<unsigned>(8 * ((g.n_rows + (8 / n_slices) - 1) / (8 / n_slices)));
+  plan->lds_bytes = static_cast<size_t>(waves) * tpw * g.capacity * 8 +
+                    static_cast<size_t>(waves) * parts_per_wave * vec * kWave * 4;
+  return true;
+}
+
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
                               const uint8_t* idx, const uint8_t* cnt, const int32_t* rows,
                               const int32_t* n_rows_dev, const void* w_down, void* y,
@@ -521,7 +431,7 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
       const uint16_t* w16 = static_cast<const uint16_t*>(w_down);
       uint16_t* y16 = static_cast<uint16_t*>(y);
       // Few rows: split each row over the 16 waves of a workgroup.
-      constexpr int P = 16;
+      constexpr int P = kSplitParts;
       const int tpw = (g.n_tiles + P - 1) / P;
       const size_t split_bytes = static_cast<size_t>(P) * tpw * g.capacity * 8 +
                                  static_cast<size_t>(P) * vec * kWave * 4;

@@ -257,10 +257,24 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
       TWELL_TRY(hipStreamWaitEvent(a->stream, a->fork, 0));
       sp = a->stream;
     }
-    TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts,
-                                 w.route.sparse_rows, w.route.n_sparse, w_down, y, sp));
+    // batches of at most 64 bf16 rows (plain call): the sparse product runs as
+    // extra workgroups of the fallback's split-K launch, inside its weight stream
+    const bool merged = ev == nullptr && eb == 2 && w.skinny != nullptr && fallback_takes_spmm(g);
+    if (merged) {
+      const SpmmRows sr{static_cast<const uint16_t*>(h_out->values), h_out->indices,
+                        h_out->counts, w.route.sparse_rows, w.route.n_sparse};
+      TWELL_TRY(launch_fallback_bf16_with_spmm(
+          g, static_cast<const uint16_t*>(h_out->dense_values), h_out->dense_rows, h_out->n_dense,
+          h_out->dense_capacity, static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y),
+          st, w.skinny, sr));
+    } else {
+      TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts,
+                                   w.route.sparse_rows, w.route.n_sparse, w_down, y, sp));
+    }
     TWELL_TRY(mark(3));
-    if (eb == 2)
+    if (merged) {
+      // done above
+    } else if (eb == 2)
       TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(h_out->dense_values),
                                      h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
                                      static_cast<const uint16_t*>(w_down),
