@@ -398,18 +398,36 @@ __global__ __launch_bounds__(NT) void materialize_slots_kernel(
   for (int i = threadIdx.x; i < nt; i += NT) cnt[slot0 + i] = 0;
 }
 
-// One wave per (row, tile) of an existing h.
-template <typename E>
+// One wave per (row, tile) of an existing h, kPackAhead (row, tile) pairs at
+// a time: the loads of all of them are issued before any is packed, so a
+// wave keeps that many tile reads in flight (one at a time left the pass
+// latency-bound at 3.3 TB/s).
+constexpr int kPackAhead = 4;
+
+template <typename E, int EPL>
 __global__ __launch_bounds__(kRowThreads) void pack_tiles_kernel(
     const E* __restrict__ h, int64_t pairs, int dff, int T, int C, int nt, E* __restrict__ vals,
     uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt, uint8_t* __restrict__ flags) {
+  const int lane = lane_id();
   const int64_t waves = static_cast<int64_t>(gridDim.x) * (kRowThreads / kWave);
-  for (int64_t q = static_cast<int64_t>(blockIdx.x) * (kRowThreads / kWave) + threadIdx.x / kWave;
-       q < pairs; q += waves) {
-    const int64_t n = q / nt;
-    const int t = static_cast<int>(q % nt);
-    pack_tile_from<E>(h + n * dff + static_cast<int64_t>(t) * T, T, C, vals + q * C, idx + q * C,
-                      cnt + q, flags + q, nullptr);
+  for (int64_t q0 = static_cast<int64_t>(blockIdx.x) * (kRowThreads / kWave) + threadIdx.x / kWave;
+       q0 < pairs; q0 += waves * kPackAhead) {
+    E v[kPackAhead][EPL];
+#pragma unroll
+    for (int u = 0; u < kPackAhead; ++u) {
+      const int64_t q = min(q0 + u * waves, pairs - 1);  // past the end: reread, not packed
+      const int64_t n = q / nt;
+      const int t = static_cast<int>(q - n * nt);
+      const E* src = h + n * dff + static_cast<int64_t>(t) * T + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) v[u][e] = src[e];
+    }
+#pragma unroll
+    for (int u = 0; u < kPackAhead; ++u) {
+      const int64_t q = q0 + u * waves;
+      if (q < pairs)
+        pack_tile<E, EPL>(v[u], C, vals + q * C, idx + q * C, cnt + q, flags + q, nullptr);
+    }
   }
 }
 
@@ -573,17 +591,20 @@ hipError_t launch_pack_tiles(const Geometry& g, const void* h, int elem_bytes, c
                              hipStream_t s) {
   const int64_t pairs = g.n_rows * g.n_tiles;
   if (pairs == 0) return hipSuccess;
-  const int64_t want = (pairs + 3) / 4;
+  const int64_t want = (pairs + 4 * kPackAhead - 1) / (4 * kPackAhead);  // 4 waves per workgroup
   const unsigned blocks = static_cast<unsigned>(want < 65536 ? want : 65536);
-  if (elem_bytes == 2) {
-    pack_tiles_kernel<uint16_t><<<blocks, kRowThreads, 0, s>>>(
-        static_cast<const uint16_t*>(h), pairs, g.d_ff, g.tile, g.capacity, g.n_tiles,
-        static_cast<uint16_t*>(out.vals), out.idx, out.cnt, out.flags);
-  } else {
-    pack_tiles_kernel<float><<<blocks, kRowThreads, 0, s>>>(
-        static_cast<const float*>(h), pairs, g.d_ff, g.tile, g.capacity, g.n_tiles,
-        static_cast<float*>(out.vals), out.idx, out.cnt, out.flags);
-  }
+  auto go = [&](auto tag, auto epl) {
+    typedef decltype(tag) E;
+    pack_tiles_kernel<E, decltype(epl)::value><<<blocks, kRowThreads, 0, s>>>(
+        static_cast<const E*>(h), pairs, g.d_ff, g.tile, g.capacity, g.n_tiles,
+        static_cast<E*>(out.vals), out.idx, out.cnt, out.flags);
+  };
+  auto by_tile = [&](auto tag) {
+    if (g.tile == 64) go(tag, std::integral_constant<int, 1>{});
+    else if (g.tile == 128) go(tag, std::integral_constant<int, 2>{});
+    else go(tag, std::integral_constant<int, 4>{});
+  };
+  if (elem_bytes == 2) by_tile(uint16_t{}); else by_tile(float{});
   return hipGetLastError();
 }
 
