@@ -26,6 +26,12 @@ constexpr int kSkKC = 256;      // K per LDS chunk of A, up-projection
 constexpr int kSkKCDown = 64;   // K per LDS chunk of A, fallback
 constexpr int kSkLoads = 16;    // weight loads a thread keeps in flight
 constexpr int kSkSumBatch = 8;  // partial-sum loads in flight per output
+// Granules of the fp32 K split: one batch of weight loads per thread (8 x 4
+// columns of a [N][K] row, 16 rows of a [K][N] weight), so a small K is cut
+// into slices that each take one round of loads instead of several in turn
+// (slice ends stay whole batches: a batch never reads past its slice).
+constexpr int kSkSliceNK = 4 * (kSkLoads / 2);
+constexpr int kSkSliceKN = kSkLoads;
 
 template <typename E>
 struct Vec16B {  // elements of E in 16 bytes
@@ -303,7 +309,7 @@ hipError_t up_f32_rows(const Geometry& g, const float* x, const float* w_up_t, c
                        const PackOut& out, float* part, hipStream_t s) {
   const int M = static_cast<int>(g.n_rows), N = g.d_ff, K = g.d_model;
   const int nb = (N + kSkThreads - 1) / kSkThreads, nz = (M + R - 1) / R;
-  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkKC, 512);
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkSliceNK, 512);
   skinny_nk_partial<float, R><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(
       x, K, M, K, N, sp.kw, sp.mm, w_up_t, part);
   const hipError_t e = hipGetLastError();
@@ -315,7 +321,7 @@ hipError_t up_f32(const Geometry& g, const float* x, const float* w_up_t, const 
                   const PackOut& out, float* part, hipStream_t s) {
   const int nb = (g.d_ff + kSkThreads - 1) / kSkThreads;
   const int nz = static_cast<int>((g.n_rows + kSkRows - 1) / kSkRows);
-  const SkinnySplit sp = skinny_split(g.n_rows, g.d_model, nb * nz, kSkKC, 512);
+  const SkinnySplit sp = skinny_split(g.n_rows, g.d_model, nb * nz, kSkSliceNK, 512);
   return nb * nz * sp.slices < kSkMinBlocks
              ? up_f32_rows<kSkRowsSmall>(g, x, w_up_t, b_up, out, part, s)
              : up_f32_rows<kSkRows>(g, x, w_up_t, b_up, out, part, s);
@@ -329,7 +335,7 @@ hipError_t fallback_f32_rows(const Geometry& g, const float* a, const int32_t* d
   const int N = g.d_model, K = g.d_ff;
   const int nb = (N + kSkThreads * CPT - 1) / (kSkThreads * CPT);
   const int nz = (m_cap + R - 1) / R;
-  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkKCDown, 512);
+  const SkinnySplit sp = skinny_split(g.n_rows, K, nb * nz, kSkSliceKN, 512);
   skinny_kn_partial<float, R><<<dim3(nb, sp.slices, nz), kSkThreads, 0, s>>>(
       a, K, n_dense, m_cap, K, N, sp.kw, sp.mm, w_down, part);
   const hipError_t e = hipGetLastError();
@@ -343,7 +349,7 @@ hipError_t fallback_f32(const Geometry& g, const float* a, const int32_t* dense_
   constexpr int CPT = kn_cols<float>();
   const int nb = (g.d_model + kSkThreads * CPT - 1) / (kSkThreads * CPT);
   const int nz = (m_cap + kSkRows - 1) / kSkRows;
-  const SkinnySplit sp = skinny_split(g.n_rows, g.d_ff, nb * nz, kSkKCDown, 512);
+  const SkinnySplit sp = skinny_split(g.n_rows, g.d_ff, nb * nz, kSkSliceKN, 512);
   return nb * nz * sp.slices < kSkMinBlocks
              ? fallback_f32_rows<kSkRowsSmall>(g, a, dense_rows, n_dense, m_cap, w_down, y, part, s)
              : fallback_f32_rows<kSkRows>(g, a, dense_rows, n_dense, m_cap, w_down, y, part, s);
