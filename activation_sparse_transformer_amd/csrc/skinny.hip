@@ -15,6 +15,8 @@
 //    (Sakana AI + NVIDIA)", Figure 1 description);
 //  dense fallback (w_down [d_ff][d_model], N-contiguous): rounding and the
 //    scatter to y[dense_rows[m]].
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -25,7 +27,9 @@ constexpr int kSkThreads = 256;
 constexpr int kSkKC = 256;      // K per LDS chunk of A, up-projection
 constexpr int kSkKCDown = 64;   // K per LDS chunk of A, fallback
 constexpr int kSkLoads = 16;    // weight loads a thread keeps in flight
-constexpr int kSkSumBatch = 8;  // partial-sum loads in flight per output
+// Partial-sum loads in flight per output: the smallest of 8, 16 and 32 that
+// covers the slice count, so the slices are read in one batch (decode layer,
+// 24 slices: three batches of 8 one after the other before).
 // Granules of the fp32 K split: one batch of weight loads per thread (8 x 4
 // columns of a [N][K] row, 16 rows of a [K][N] weight), so a small K is cut
 // into slices that each take one round of loads instead of several in turn
@@ -206,26 +210,26 @@ __global__ __launch_bounds__(kSkThreads) void skinny_nk_partial(
     if (r0 + m < M) dst[static_cast<int64_t>(m) * N] = acc[m];
 }
 
-// Sum over slices of part[slice][m][n] (slice stride `stride`), in slice
-// order, kSkSumBatch loads in flight.
+// Sum over the ks <= B slices of part[slice][m][n] (slice stride `stride`),
+// in slice order, with all B loads issued before the first add (loads past
+// the last slice reread it and are dropped).
+template <int B>
 __device__ __forceinline__ float slice_sum(const float* __restrict__ p, int ks, int64_t stride) {
+  float v[B];
+#pragma unroll
+  for (int u = 0; u < B; ++u) v[u] = p[static_cast<int64_t>(min(u, ks - 1)) * stride];
+  // a scheduling boundary: without it the adds are moved up between the
+  // loads and only 8 loads stay in flight
+  asm volatile("" ::: "memory");
   float s = 0.f;
-  for (int kc = 0; kc < ks; kc += kSkSumBatch) {
-    float v[kSkSumBatch];
 #pragma unroll
-    for (int u = 0; u < kSkSumBatch; ++u) {
-      const int q = kc + u < ks ? kc + u : kc;  // past the end: reread, then drop
-      v[u] = p[q * stride];
-    }
-#pragma unroll
-    for (int u = 0; u < kSkSumBatch; ++u)
-      if (kc + u < ks) s += v[u];
-  }
+  for (int u = 0; u < B; ++u)
+    if (u < ks) s += v[u];
   return s;
 }
 
 // Fallback epilogue: y[dense_rows[m]][n] = sum over slices, rounded.
-template <typename E>
+template <typename E, int B>
 __global__ __launch_bounds__(kSkThreads) void skinny_fallback_reduce(
     const float* __restrict__ part, int ks, int mm, const int32_t* __restrict__ n_dense,
     int m_cap, const int32_t* __restrict__ dense_rows, int64_t y_rows, int N, E* __restrict__ y) {
@@ -233,7 +237,8 @@ __global__ __launch_bounds__(kSkThreads) void skinny_fallback_reduce(
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kSkThreads + threadIdx.x;
   if (i >= static_cast<int64_t>(M) * N) return;
   const int m = static_cast<int>(i / N), n = static_cast<int>(i - static_cast<int64_t>(m) * N);
-  const float s = slice_sum(part + static_cast<int64_t>(m) * N + n, ks, static_cast<int64_t>(mm) * N);
+  const float s =
+      slice_sum<B>(part + static_cast<int64_t>(m) * N + n, ks, static_cast<int64_t>(mm) * N);
   const int64_t r = dense_rows[m];
   if (r >= 0 && r < y_rows) y[r * N + n] = ElemTraits<E>::from_f32(s);
 }
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_fallback_reduce(
 // w packs row 4 blockIdx.y + w of the tile.
 constexpr int kPackRows = kSkThreads / kWave;
 
-template <typename E>
+template <typename E, int B>
 __global__ __launch_bounds__(kSkThreads) void skinny_up_pack(
     const float* __restrict__ part, int ks, int mm, int M, int dff, int T, int C, int nt,
     const float* __restrict__ bias, E* __restrict__ vals, uint8_t* __restrict__ idx,
@@ -256,6 +261,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_up_pack(
   const int c0 = t * T;
   const int64_t stride = static_cast<int64_t>(mm) * dff;
   // all slice loads of all of this thread's elements in flight together
+  // (the launcher picks B >= ks)
   float z[EPT];
   int64_t off[EPT];
   bool ok[EPT];
@@ -267,20 +273,18 @@ __global__ __launch_bounds__(kSkThreads) void skinny_up_pack(
     off[j] = static_cast<int64_t>(ok[j] ? r0 + m : r0) * dff + c0 + (ok[j] ? c : 0);
     z[j] = 0.f;
   }
-  for (int kc = 0; kc < ks; kc += kSkSumBatch) {
-    float v[EPT][kSkSumBatch];
+  {  // ks <= B: one batch; loads past the last slice reread it and are dropped
+    float v[EPT][B];
 #pragma unroll
     for (int j = 0; j < EPT; ++j)
 #pragma unroll
-      for (int u = 0; u < kSkSumBatch; ++u) {
-        const int q = kc + u < ks ? kc + u : kc;  // past the end: reread, then drop
-        v[j][u] = part[q * stride + off[j]];
-      }
+      for (int u = 0; u < B; ++u) v[j][u] = part[min(u, ks - 1) * stride + off[j]];
+    asm volatile("" ::: "memory");  // every load issued before the first add
 #pragma unroll
     for (int j = 0; j < EPT; ++j)
 #pragma unroll
-      for (int u = 0; u < kSkSumBatch; ++u)
-        if (kc + u < ks) z[j] += v[j][u];
+      for (int u = 0; u < B; ++u)
+        if (u < ks) z[j] += v[j][u];
   }
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
@@ -357,6 +361,15 @@ hipError_t fallback_f32(const Geometry& g, const float* a, const int32_t* dense_
 
 }  // namespace
 
+// Calls f with the partial-sum batch for `slices` slices (at most 32).
+template <class F>
+void by_sum_batch(int slices, F&& f) {
+  static_assert(kSkinnyMaxSlices <= 32, "one batch of 32 covers every slice count");
+  if (slices <= 8) f(std::integral_constant<int, 8>{});
+  else if (slices <= 16) f(std::integral_constant<int, 16>{});
+  else f(std::integral_constant<int, 32>{});
+}
+
 SkinnySplit skinny_split(int64_t n_rows, int K, int n_blocks, int granule, int target_blocks) {
   int want = (target_blocks + n_blocks - 1) / n_blocks;
   want = want < 1 ? 1 : want > kSkinnyMaxSlices ? kSkinnyMaxSlices : want;
@@ -377,10 +390,13 @@ hipError_t launch_skinny_up_epilogue(const Geometry& g, const SkinnySplit& sp, c
                                      const float* b_up, const PackOut& out, hipStream_t s) {
   if (g.tile > 256) return hipErrorInvalidValue;  // the tile is staged in LDS
   const unsigned groups = static_cast<unsigned>((g.n_rows + kPackRows - 1) / kPackRows);
-  skinny_up_pack<E><<<dim3(g.n_tiles, groups), kSkThreads, 0, s>>>(
-      part, sp.slices, sp.mm, static_cast<int>(g.n_rows), g.d_ff, g.tile, g.capacity, g.n_tiles,
-      b_up, static_cast<E*>(out.vals), out.idx, out.cnt, out.flags, static_cast<E*>(out.spill),
-      static_cast<E*>(out.h_debug));
+  auto go = [&](auto b) {
+    skinny_up_pack<E, decltype(b)::value><<<dim3(g.n_tiles, groups), kSkThreads, 0, s>>>(
+        part, sp.slices, sp.mm, static_cast<int>(g.n_rows), g.d_ff, g.tile, g.capacity,
+        g.n_tiles, b_up, static_cast<E*>(out.vals), out.idx, out.cnt, out.flags,
+        static_cast<E*>(out.spill), static_cast<E*>(out.h_debug));
+  };
+  by_sum_batch(sp.slices, go);
   return hipGetLastError();
 }
 
@@ -389,9 +405,12 @@ hipError_t launch_skinny_fallback_reduce(const Geometry& g, const SkinnySplit& s
                                          const float* part, const int32_t* n_dense, int m_cap,
                                          const int32_t* dense_rows, E* y, hipStream_t s) {
   const int64_t outs = static_cast<int64_t>(m_cap) * g.d_model;
-  skinny_fallback_reduce<E><<<static_cast<unsigned>((outs + kSkThreads - 1) / kSkThreads),
-                              kSkThreads, 0, s>>>(part, sp.slices, sp.mm, n_dense, m_cap,
-                                                  dense_rows, g.n_rows, g.d_model, y);
+  auto go = [&](auto b) {
+    skinny_fallback_reduce<E, decltype(b)::value>
+        <<<static_cast<unsigned>((outs + kSkThreads - 1) / kSkThreads), kSkThreads, 0, s>>>(
+            part, sp.slices, sp.mm, n_dense, m_cap, dense_rows, g.n_rows, g.d_model, y);
+  };
+  by_sum_batch(sp.slices, go);
   return hipGetLastError();
 }
 
