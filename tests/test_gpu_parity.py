@@ -374,6 +374,41 @@ def test_forward_matches_standalone_pack_and_spmm():
     np.testing.assert_array_equal(u32(as_f32(out.y)), u32(as_f32(y2)))
 
 
+@pytest.mark.parametrize("n_rows,d_model,d_ff", [(64, 128, 512), (45, 72, 320), (33, 512, 2560),
+                                                 (7, 264, 1088)])
+def test_forward_fp32_small_batch_matches_timed_and_standalone(n_rows, d_model, d_ff):
+    """float32, at most 64 rows (split-K partial sums, rows routed inside the
+    dense-row build, the 16-range few-row sparse kernel): the plain call and
+    the event-timed variant give the same y bit for bit; twell_spmm on the
+    standalone pack of the same h gives the same bits on the sparse rows (one
+    and several column chunks and tiles per range) and runs the dense rows
+    through its own fallback kernel, having no workspace for split-K partial
+    sums (checked against the oracle)."""
+    cfg = CONFIGS["tiny_fp32"].replace(n_rows=n_rows, d_model=d_model, d_ff=d_ff)
+    say(f"fp32 small batch n={n_rows} dm={d_model} dff={d_ff}")
+    t = make_inputs(cfg)
+    d = inputs_to_device(t)
+    a = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
+                                 cfg.capacity, debug_h=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    b = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
+                                 cfg.capacity, stage_events=evs)
+    torch.cuda.synchronize()
+    assert int(a.status.item()) == twell.TWELL_OK
+    assert a.hybrid.n_dense_host() < cfg.n_rows  # some rows go through the sparse product
+    hy, _ = twell.twell_pack(a.h_debug, cfg.tile, cfg.capacity)
+    y2 = twell.twell_spmm(hy, d["w_down"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(u32(as_f32(a.y)), u32(as_f32(b.y)))
+    nd = a.hybrid.n_dense_host()
+    sparse = np.ones(cfg.n_rows, dtype=bool)
+    sparse[a.hybrid.dense_rows[:nd].cpu().numpy()] = False
+    np.testing.assert_array_equal(u32(as_f32(a.y))[sparse], u32(as_f32(y2))[sparse])
+    _, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    assert_close_rel(as_f64(a.y), y_ref, TOL[cfg.torch_dtype], "y")
+    assert_close_rel(as_f64(y2), y_ref, TOL[cfg.torch_dtype], "twell_spmm y")
+
+
 @pytest.mark.parametrize("n_rows", [16, 48, 700, 1500, 2600])
 def test_forward_timed_variant_matches_plain_call(n_rows):
     """The event-recording variant (every stage in order on the stream) and the
