@@ -102,10 +102,24 @@ struct RouteOut {
   const uint8_t* row_dense;
 };
 
+// The down-projection operands of a dense-row build that also runs the
+// sparse product of the sparse rows (float32, at most 64 rows).
+struct BuildSpmm {
+  const void* w_down;
+  void* y;
+};
+
+// Whether launch_route_materialize can take a BuildSpmm for this shape: float32,
+// the rows routed inside the build (route_mode 1), rows built in LDS, and a
+// shape for which launch_spmm_sparse would run the 16-range few-row kernel, so
+// that y is the same bits either way.
+bool build_takes_spmm(const Geometry& g, int elem_bytes);
+
 hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* row_map,
                               const uint8_t* flags, const void* spill, const void* full_src,
                               void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
-                              int64_t dense_cap, hipStream_t s, const RouteOut* route = nullptr);
+                              int64_t dense_cap, hipStream_t s, const RouteOut* route = nullptr,
+                              const BuildSpmm* sp = nullptr);
 
 // G2 without the scan kernel: route_mode says whether the dense-row build can
 // route the rows itself (1: at most 64 rows, each workgroup ORs every row's
@@ -119,7 +133,8 @@ hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const Rou
                                     const void* spill, const void* full_src, void* vals,
                                     uint8_t* idx, uint8_t* cnt, int32_t* dense_rows,
                                     void* dense_values, int64_t dense_cap, int32_t* n_dense,
-                                    int32_t* status, hipStream_t s);
+                                    int32_t* status, hipStream_t s,
+                                    const BuildSpmm* sp = nullptr);
 
 // G6: twell_to_dense.
 hipError_t launch_unpack(const Geometry& g, int elem_bytes, const void* vals, const uint8_t* idx,

@@ -23,6 +23,7 @@
 #include "../../include/twell.h"
 #include "common.h"
 #include "kernels.h"
+#include "spmm_split.h"
 
 namespace twell {
 namespace {
@@ -245,30 +246,51 @@ __device__ __forceinline__ int row_dense_index(const RouteOut& ro, const int32_t
 // stored slots scattered in), then written out 16 bytes per thread, taking the
 // overflowing tiles from the spill area; with `full_src` the row is copied
 // from h as is.  Finally the row's TwELL slots are cleared.
-template <typename E, bool IN_LDS, int RM>
-__global__ __launch_bounds__(kRowThreads) void materialize_kernel(
+//
+// With `sp.w_down` set (float32, rows routed in the workgroup, built in LDS,
+// 1024 threads), a sparse row's workgroup computes the row's y instead of
+// leaving: its 16 waves take the row's 16 tile ranges, as the separate few-row
+// sparse kernel does, so y is the same bits.  sp_dm, sp_tpw, sp_chunks:
+// d_model, tiles per range, 64-lane column chunks.
+template <typename E, bool IN_LDS, int RM, int NT = kRowThreads>
+__global__ __launch_bounds__(NT) void materialize_kernel(
     int dff, int T, int C, int nt, const int32_t* __restrict__ row_map,
     const uint8_t* __restrict__ flags, const E* __restrict__ spill, const E* __restrict__ full_src,
     E* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
-    E* __restrict__ dense_values, int64_t cap, RouteOut ro) {
+    E* __restrict__ dense_values, int64_t cap, RouteOut ro, BuildSpmm sp, int sp_dm, int sp_tpw,
+    int sp_chunks) {
   constexpr int V = Vec16<E>::N;
   extern __shared__ __attribute__((aligned(16))) unsigned char mat_lds[];
   E* rowbuf = reinterpret_cast<E*>(mat_lds);
   const int64_t n = blockIdx.x;
   const int m = row_dense_index<RM>(ro, row_map, flags, nt, cap, n);
-  if (m < 0) return;
+  if (m < 0) {
+    if constexpr (IN_LDS && RM == 1 && NT == kSplitParts * kWave &&
+                  std::is_same<E, float>::value) {
+      if (sp.w_down != nullptr) {
+        uint2* lists = reinterpret_cast<uint2*>(mat_lds);
+        float* red = reinterpret_cast<float*>(lists + kSplitParts * sp_tpw * C);
+        for (int chunk = 0; chunk < sp_chunks; ++chunk)
+          spmm_split_row_chunk<E, kSplitParts, 1>(vals, idx, cnt, n,
+                                                  static_cast<const E*>(sp.w_down),
+                                                  static_cast<E*>(sp.y), sp_dm, T, C, nt, sp_tpw,
+                                                  chunk, lists, red);
+      }
+    }
+    return;
+  }
   const int64_t slot0 = n * nt;
   const int nslots = nt * C;
   if (m < cap) {
     E* dst = dense_values + static_cast<int64_t>(m) * dff;
     if (full_src != nullptr) {
-      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+      for (int c = threadIdx.x * V; c < dff; c += NT * V) {
         Vec16<E> o;
         load_vec(o, full_src + n * dff + c);
         store_vec(dst + c, o);
       }
     } else if (!IN_LDS) {  // row too long for LDS: rebuild each 16 bytes from the tile's slots
-      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+      for (int c = threadIdx.x * V; c < dff; c += NT * V) {
         Vec16<E> o;
         const int t = c / T;
         if (flags[slot0 + t]) {
@@ -280,14 +302,14 @@ __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
         store_vec(dst + c, o);
       }
     } else {
-      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+      for (int c = threadIdx.x * V; c < dff; c += NT * V) {
         Vec16<E> z;
 #pragma unroll
         for (int i = 0; i < V; ++i) z.v[i] = E(0);
         store_vec(rowbuf + c, z);
       }
       __syncthreads();
-      for (int s = threadIdx.x; s < nslots; s += kRowThreads) {
+      for (int s = threadIdx.x; s < nslots; s += NT) {
         const int t = s / C;
         // count, index and value loaded together: no load waits on another
         const int count = cnt[slot0 + t];
@@ -296,7 +318,7 @@ __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
         if (s - t * C < count && local < T) rowbuf[t * T + local] = v;
       }
       __syncthreads();
-      for (int c = threadIdx.x * V; c < dff; c += kRowThreads * V) {
+      for (int c = threadIdx.x * V; c < dff; c += NT * V) {
         // a plain 16-byte value (an array loaded from either address space
         // would be kept in scratch memory)
         const uint4 o = flags[slot0 + c / T] ? *reinterpret_cast<const uint4*>(spill + n * dff + c)
@@ -306,11 +328,11 @@ __global__ __launch_bounds__(kRowThreads) void materialize_kernel(
     }
   }
   __syncthreads();  // every read of this row's slots is done before they are cleared
-  for (int64_t i = threadIdx.x; i < nslots; i += kRowThreads) {
+  for (int64_t i = threadIdx.x; i < nslots; i += NT) {
     vals[slot0 * C + i] = E(0);
     idx[slot0 * C + i] = 0;
   }
-  for (int i = threadIdx.x; i < nt; i += kRowThreads) cnt[slot0 + i] = 0;
+  for (int i = threadIdx.x; i < nt; i += NT) cnt[slot0 + i] = 0;
 }
 
 // Dense-row build for capacities of 4 or 8 slots: one workgroup per row,
@@ -507,7 +529,7 @@ hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const Rou
                                     const void* spill, const void* full_src, void* vals,
                                     uint8_t* idx, uint8_t* cnt, int32_t* dense_rows,
                                     void* dense_values, int64_t dense_cap, int32_t* n_dense,
-                                    int32_t* status, hipStream_t s) {
+                                    int32_t* status, hipStream_t s, const BuildSpmm* sp) {
   const int mode = route_mode(g);
   if (mode == 0) return hipErrorInvalidValue;
   if (mode == 2) {
@@ -517,14 +539,61 @@ hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const Rou
   const RouteOut ro{g.n_rows, dense_rows, n_dense, rb.sparse_rows, rb.n_sparse, status,
                     mode == 2 ? rb.row_dense : nullptr};
   return launch_materialize(g, elem_bytes, nullptr, rb.flags, spill, full_src, vals, idx, cnt,
-                            dense_values, dense_cap, s, &ro);
+                            dense_values, dense_cap, s, &ro, sp);
+}
+
+namespace {
+// The few-row sparse product as a float32 dense-row build runs it: 16 waves,
+// one tile range each, and the LDS for their slot lists and range sums.
+struct BuildSpmmPlan {
+  int tpw, n_chunks;
+  size_t lds_bytes;
+};
+BuildSpmmPlan build_spmm_plan(const Geometry& g) {
+  constexpr int V = 4;  // float32 columns per lane
+  BuildSpmmPlan pl;
+  pl.tpw = (g.n_tiles + kSplitParts - 1) / kSplitParts;
+  pl.n_chunks = (g.d_model + kWave * V - 1) / (kWave * V);
+  pl.lds_bytes = static_cast<size_t>(kSplitParts) * pl.tpw * g.capacity * 8 +
+                 static_cast<size_t>(kSplitParts) * V * kWave * 4;
+  return pl;
+}
+}  // namespace
+
+bool build_takes_spmm(const Geometry& g, int elem_bytes) {
+  if (elem_bytes != 4 || g.n_rows <= 0 || route_mode(g) != 1) return false;
+  const size_t row_bytes = static_cast<size_t>(g.d_ff) * 4;
+  // launch_materialize's choice: slot groups for long rows of 4 or 8 slots,
+  // no LDS row buffer past 64 KB
+  if ((g.capacity == 4 || g.capacity == 8) && row_bytes > 20 * 1024) return false;
+  if (row_bytes > 64 * 1024) return false;
+  // launch_spmm_sparse's choice of the 16-range kernel for float32 (same LDS)
+  const BuildSpmmPlan pl = build_spmm_plan(g);
+  return g.n_rows * pl.n_chunks <= 1024 && pl.lds_bytes <= 64 * 1024;
 }
 
 hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* row_map,
                               const uint8_t* flags, const void* spill, const void* full_src,
                               void* vals, uint8_t* idx, uint8_t* cnt, void* dense_values,
-                              int64_t dense_cap, hipStream_t s, const RouteOut* route) {
+                              int64_t dense_cap, hipStream_t s, const RouteOut* route,
+                              const BuildSpmm* sp) {
   if (g.n_rows == 0) return hipSuccess;
+  if (sp != nullptr) {
+    // float32, routed in the workgroup, built in LDS: 1024 threads per row
+    if (!build_takes_spmm(g, elem_bytes) || route == nullptr || route->row_dense != nullptr ||
+        full_src != nullptr)
+      return hipErrorInvalidValue;
+    const BuildSpmmPlan pl = build_spmm_plan(g);
+    const size_t row_bytes = static_cast<size_t>(g.d_ff) * 4;
+    const size_t lds = pl.lds_bytes > row_bytes ? pl.lds_bytes : row_bytes;
+    materialize_kernel<float, true, 1, kSplitParts * kWave>
+        <<<static_cast<unsigned>(g.n_rows), kSplitParts * kWave, lds, s>>>(
+            g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
+            static_cast<const float*>(spill), nullptr, static_cast<float*>(vals), idx, cnt,
+            static_cast<float*>(dense_values), dense_cap, *route, *sp, g.d_model, pl.tpw,
+            pl.n_chunks);
+    return hipGetLastError();
+  }
   // 0: the scan's row map; 1: routed inside each workgroup; 2: counted from row_dense
   const int rmode = route == nullptr ? 0 : route->row_dense == nullptr ? 1 : 2;
   const RouteOut ro = route != nullptr ? *route : RouteOut{};
@@ -572,7 +641,8 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
         <<<blocks, kRowThreads, lds, s>>>(g.d_ff, g.tile, g.capacity, g.n_tiles, row_map, flags,
                                           static_cast<const E*>(spill),
                                           static_cast<const E*>(full_src), static_cast<E*>(vals),
-                                          idx, cnt, static_cast<E*>(dense_values), dense_cap, ro);
+                                          idx, cnt, static_cast<E*>(dense_values), dense_cap, ro,
+                                          BuildSpmm{nullptr, nullptr}, 0, 0, 0);
   };
   typedef std::integral_constant<bool, true> Yes;
   typedef std::integral_constant<bool, false> No;

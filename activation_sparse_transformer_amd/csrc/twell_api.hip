@@ -145,15 +145,18 @@ AuxStream* aux_stream(hipError_t* err) {
 
 // Steps 2-4 of the forward pass once the pack step has run: route, build
 // the dense rows, sparse product, dense fallback.
+// With `sp` (build_takes_spmm held), the build also runs the sparse product.
 int route_and_materialize(const Geometry& g, int eb, const PackWorkspace& w, const void* full_src,
-                          const twell_hybrid* hy, int32_t* d_status, hipStream_t st) {
+                          const twell_hybrid* hy, int32_t* d_status, hipStream_t st,
+                          const BuildSpmm* sp = nullptr) {
   if (route_mode(g) != 0) {
     // the dense-row build routes the rows itself: no scan kernel
     TWELL_TRY(launch_route_materialize(g, eb, w.route, w.spill, full_src, hy->values,
                                        hy->indices, hy->counts, hy->dense_rows, hy->dense_values,
-                                       hy->dense_capacity, hy->n_dense, d_status, st));
+                                       hy->dense_capacity, hy->n_dense, d_status, st, sp));
     return TWELL_OK;
   }
+  if (sp != nullptr) return TWELL_ERR_INVALID_ARG;
   TWELL_TRY(launch_route_scan(g, w.route, hy->dense_rows, hy->dense_capacity, hy->n_dense,
                               d_status, st));
   TWELL_TRY(launch_materialize(g, eb, w.route.row_map, w.route.flags, w.spill, full_src, hy->values,
@@ -235,8 +238,14 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
                                    static_cast<const float*>(w_up_t), b_up, po, st));
   }
   TWELL_TRY(mark(1));
-  // 2. route rows, build dense rows from the TwELL slots + spilled tiles
-  if ((rc = route_and_materialize(g, eb, w, nullptr, h_out, d_status, st)) != TWELL_OK) return rc;
+  // 2. route rows, build dense rows from the TwELL slots + spilled tiles; for
+  // float32 batches of at most 64 rows (plain call) the build's sparse-row
+  // workgroups also run step 3 for their rows
+  const bool build_spmm = ev == nullptr && g.n_rows > 0 && build_takes_spmm(g, eb);
+  const BuildSpmm bsp{w_down, y};
+  if ((rc = route_and_materialize(g, eb, w, nullptr, h_out, d_status, st,
+                                  build_spmm ? &bsp : nullptr)) != TWELL_OK)
+    return rc;
   TWELL_TRY(mark(2));
   // 3. sparse down-projection of the TwELL rows and 4. dense fallback for the
   // dense rows.  They write disjoint rows of y: the plain call runs 3 on the
@@ -267,7 +276,7 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
           g, static_cast<const uint16_t*>(h_out->dense_values), h_out->dense_rows, h_out->n_dense,
           h_out->dense_capacity, static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y),
           st, w.skinny, sr));
-    } else {
+    } else if (!build_spmm) {
       TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts,
                                    w.route.sparse_rows, w.route.n_sparse, w_down, y, sp));
     }

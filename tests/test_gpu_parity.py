@@ -377,13 +377,13 @@ def test_forward_matches_standalone_pack_and_spmm():
 @pytest.mark.parametrize("n_rows,d_model,d_ff", [(64, 128, 512), (45, 72, 320), (33, 512, 2560),
                                                  (7, 264, 1088)])
 def test_forward_fp32_small_batch_matches_timed_and_standalone(n_rows, d_model, d_ff):
-    """float32, at most 64 rows (split-K partial sums, rows routed inside the
-    dense-row build, the 16-range few-row sparse kernel): the plain call and
-    the event-timed variant give the same y bit for bit; twell_spmm on the
-    standalone pack of the same h gives the same bits on the sparse rows (one
-    and several column chunks and tiles per range) and runs the dense rows
-    through its own fallback kernel, having no workspace for split-K partial
-    sums (checked against the oracle)."""
+    """float32, at most 64 rows: the plain call runs the sparse product inside
+    the dense-row build (its sparse rows' 16-wave workgroups, one tile range
+    per wave), the event-timed variant as its own 16-range kernel. y is the
+    same bits both ways; twell_spmm on the standalone pack of the same h gives
+    the same bits on the sparse rows (one and several column chunks and tiles
+    per range) and runs the dense rows through its own fallback kernel, having
+    no workspace for split-K partial sums (checked against the oracle)."""
     cfg = CONFIGS["tiny_fp32"].replace(n_rows=n_rows, d_model=d_model, d_ff=d_ff)
     say(f"fp32 small batch n={n_rows} dm={d_model} dff={d_ff}")
     t = make_inputs(cfg)
