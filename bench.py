@@ -54,10 +54,14 @@ STAGE_KERNELS = {
 # sources of each stage's kernels: a recorded traffic figure stands only while they are unchanged
 _CSRC = "activation_sparse_transformer_amd/csrc/"
 STAGE_SOURCES = {
-    "up_gemm_pack": (_CSRC + "gemm_bf16.hip", _CSRC + "common.h"),
-    "route": (_CSRC + "route.hip", _CSRC + "common.h"),
-    "spmm_sparse": (_CSRC + "spmm.hip", _CSRC + "common.h"),
-    "fallback_gemm": (_CSRC + "gemm_bf16.hip", _CSRC + "common.h"),
+    "up_gemm_pack": (_CSRC + "gemm_bf16.hip", _CSRC + "common.h", _CSRC + "kernels.h",
+                     _CSRC + "spmm_split.h"),
+    "route": (_CSRC + "route.hip", _CSRC + "common.h", _CSRC + "kernels.h",
+              _CSRC + "spmm_split.h"),
+    "spmm_sparse": (_CSRC + "spmm.hip", _CSRC + "common.h", _CSRC + "kernels.h",
+                    _CSRC + "spmm_split.h"),
+    "fallback_gemm": (_CSRC + "gemm_bf16.hip", _CSRC + "common.h", _CSRC + "kernels.h",
+                      _CSRC + "spmm_split.h"),
 }
 
 
