@@ -148,7 +148,9 @@ size_t ffn_sparse_workspace_size(const twell_shape* shape);
  * forked from and joined back into `stream` with events, so all work still
  * completes in `stream` order and the pass can be captured into a HIP graph
  * from `stream`.  Calls on one device share that auxiliary stream.  For at
- * most 64 rows both run in order on `stream`.
+ * most 64 rows both run in order on `stream`; step 3 may then share a launch with
+ * step 4 (bf16) or with step 2's dense-row build (float32, rows of at most
+ * 64 KB, when the shape allows), computing the same bits as when it runs alone.
  * Arguments: shape (host pointer); x, w_up_t, b_up, w_down inputs; y output;
  * h_out (host pointer to a struct of device pointers) receives h in hybrid
  * TwELL form; h_dense_debug, if non-NULL, receives h [n_rows][d_ff] exactly
