@@ -135,6 +135,22 @@ __device__ __forceinline__ void pack_tile_from(const E* src, int T, int C, E* va
   }
 }
 
+// ------------------------------------------------------------ row lists
+// Whether row n is one of the stored dense rows dense_rows[0 .. min(*n_dense,
+// cap)), which are strictly ascending: a binary search (cap 0: never).
+__device__ __forceinline__ bool listed_dense(int64_t n, const int32_t* __restrict__ dense_rows,
+                                             const int32_t* __restrict__ n_dense, int64_t cap) {
+  if (cap <= 0) return false;
+  const int64_t stored = min(static_cast<int64_t>(max(*n_dense, 0)), cap);
+  int64_t lo = 0, hi = stored;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (static_cast<int64_t>(dense_rows[mid]) < n) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo < stored && static_cast<int64_t>(dense_rows[lo]) == n;
+}
+
 // ------------------------------------------------------------ misc
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);

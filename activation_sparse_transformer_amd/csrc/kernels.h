@@ -141,12 +141,21 @@ hipError_t launch_unpack(const Geometry& g, int elem_bytes, const void* vals, co
                          const uint8_t* cnt, const int32_t* dense_rows, const void* dense_values,
                          const int32_t* n_dense, int64_t dense_cap, void* h, hipStream_t s);
 
+// Rows the sparse product leaves alone when it walks every row: the stored
+// dense rows dense_rows[0 .. min(*n_dense, cap)), ascending (cap 0: none).
+struct DenseSkip {
+  const int32_t* dense_rows;
+  const int32_t* n_dense;
+  int64_t cap;
+};
+
 // G3: y[n] = sum of value * w_down[row] over the stored slots of row n, for
-// the rows rows[0 .. *n_rows_dev) when `rows` is given, else for every row.
+// the rows rows[0 .. *n_rows_dev) when `rows` is given, else for every row
+// that `skip` (may be null) does not list.
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
                               const uint8_t* idx, const uint8_t* cnt, const int32_t* rows,
-                              const int32_t* n_rows_dev, const void* w_down, void* y,
-                              hipStream_t s);
+                              const int32_t* n_rows_dev, const DenseSkip* skip,
+                              const void* w_down, void* y, hipStream_t s);
 
 // G4: y[dense_rows[m]] = dense_values[m] w_down for m < min(*n_dense, dense_cap).
 // `skinny`: skinny_ws_bytes(g) of workspace for the split-K path, or nullptr.

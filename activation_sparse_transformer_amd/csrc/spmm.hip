@@ -46,7 +46,7 @@ __device__ __forceinline__ uint4 store_form<float>(const float (&acc)[4]) {
 template <typename E>
 __global__ __launch_bounds__(kThreads) void spmm_sparse_kernel(
     const E* __restrict__ vals, const uint8_t* __restrict__ idx, const uint8_t* __restrict__ cnt,
-    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_dev,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_dev, DenseSkip skip,
     const E* __restrict__ w, E* __restrict__ y, int64_t N, int dm, int T, int C, int nt,
     int n_chunks) {
   constexpr int V = SpmmVec<E>::N;
@@ -61,6 +61,7 @@ __global__ __launch_bounds__(kThreads) void spmm_sparse_kernel(
     const int chunk = static_cast<int>(item / R);
     const int64_t k = item % R;
     const int64_t n = rows != nullptr ? rows[k] : k;  // a listed (sparse) row, or every row
+    if (rows == nullptr && listed_dense(n, skip.dense_rows, skip.n_dense, skip.cap)) continue;
     const int col = chunk * (kWave * V) + lane * V;
     const bool live_col = col < dm;
     float acc[V];
@@ -206,7 +207,7 @@ template <int VEC, int SPL>
 __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
     const uint16_t* __restrict__ vals, const uint8_t* __restrict__ idx,
     const uint8_t* __restrict__ cnt, const int32_t* __restrict__ rows,
-    const int32_t* __restrict__ n_rows_dev, const uint16_t* __restrict__ w,
+    const int32_t* __restrict__ n_rows_dev, DenseSkip skip, const uint16_t* __restrict__ w,
     uint16_t* __restrict__ y, int64_t N, int dm, int T, int C, int nt, int n_slices) {
   extern __shared__ uint2 spmm_lists[];
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -223,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void spmm_list_bf16_kernel(
   const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
   for (int64_t k = part + parts * wid; k < R; k += parts * per_xcd_waves) {
     const int64_t n = rows != nullptr ? rows[k] : k;
+    if (rows == nullptr && listed_dense(n, skip.dense_rows, skip.n_dense, skip.cap)) continue;
     const int nnz = compact_row<SPL>(vals, idx, cnt, n, nt, C, T, dm, nslots, list);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's list is in LDS
     float acc[VEC];
@@ -265,11 +267,11 @@ template <int VEC, int P>
 __global__ __launch_bounds__(P * kWave) void spmm_split_bf16_kernel(
     const uint16_t* __restrict__ vals, const uint8_t* __restrict__ idx,
     const uint8_t* __restrict__ cnt, const int32_t* __restrict__ rows,
-    const int32_t* __restrict__ n_rows_dev, const uint16_t* __restrict__ w,
+    const int32_t* __restrict__ n_rows_dev, DenseSkip skip, const uint16_t* __restrict__ w,
     uint16_t* __restrict__ y, int64_t N, int dm, int T, int C, int nt, int n_slices, int tpw) {
   extern __shared__ uint2 spmm_lists[];
   spmm_split_rows<VEC, P>(vals, idx, cnt, rows, n_rows_dev, w, y, N, dm, T, C, nt, n_slices, tpw,
-                          spmm_lists, blockIdx.x, gridDim.x);
+                          spmm_lists, blockIdx.x, gridDim.x, skip);
 }
 
 // Few rows, float32 (or a d_model the XCD-sliced kernel does not take): one
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(P * kWave) void spmm_split_bf16_kernel(
 template <typename E, int P>
 __global__ __launch_bounds__(P * kWave) void spmm_split_kernel(
     const E* __restrict__ vals, const uint8_t* __restrict__ idx, const uint8_t* __restrict__ cnt,
-    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_dev,
+    const int32_t* __restrict__ rows, const int32_t* __restrict__ n_rows_dev, DenseSkip skip,
     const E* __restrict__ w, E* __restrict__ y, int64_t N, int dm, int T, int C, int nt,
     int n_chunks, int tpw) {
   extern __shared__ uint2 spmm_lists[];
@@ -287,136 +289,160 @@ __global__ __launch_bounds__(P * kWave) void spmm_split_kernel(
   const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
   for (int64_t k = blockIdx.x; k < R; k += gridDim.x) {
     const int64_t n = rows != nullptr ? rows[k] : k;
+    if (rows == nullptr && listed_dense(n, skip.dense_rows, skip.n_dense, skip.cap)) continue;
     spmm_split_row_chunk<E, P, 1>(vals, idx, cnt, n, w, y, dm, T, C, nt, tpw, blockIdx.y,
                                   spmm_lists, red);
   }
 }
 
+// The one place the sparse product's kernel is chosen (launch_spmm_sparse,
+// and the kernels that run its few-row form inside another launch).
+enum class SpmmKind {
+  kSplitSliced,  // bf16, few rows: 16 waves per (row, XCD column slice)
+  kListSliced,   // bf16: one wave per (row, XCD column slice), slot list in LDS
+  kSplitChunk,   // few rows, other widths or float32: 16 waves per (row, 64-lane chunk)
+  kWaveChunk,    // anything else: one wave per (row, 64-lane chunk)
+};
+struct SpmmPlan {
+  SpmmKind kind;
+  int n_slices, vec;  // sliced kinds: column slices, bf16 per lane
+  int n_chunks;       // chunk kinds: 64-lane column chunks
+  int tpw;            // split kinds: tiles per range
+  int spl;            // kListSliced: slots per lane when a row's slots fill whole waves, else 0
+  unsigned blocks;
+  size_t lds_bytes;
+};
+
+SpmmPlan spmm_plan(const Geometry& g, int elem_bytes) {
+  SpmmPlan p{};
+  const int V = elem_bytes == 2 ? SpmmVec<uint16_t>::N : SpmmVec<float>::N;
+  p.n_chunks = (g.d_model + kWave * V - 1) / (kWave * V);
+  constexpr int P = kSplitParts;
+  p.tpw = (g.n_tiles + P - 1) / P;
+  const size_t split_lists = static_cast<size_t>(P) * p.tpw * g.capacity * 8;
+  if (elem_bytes == 2 && g.d_model % 512 == 0) {
+    // Column slices of 64 lanes x 8 bf16 (x 16 when d_model/8 needs it), one
+    // per XCD or shared by 2, 4, 8 XCDs; slot lists must fit in LDS, and
+    // w_down byte offsets in 32 bits.
+    const int ns = g.d_model / 512;
+    if (ns == 1 || ns == 2 || ns == 4 || ns == 8) p.n_slices = ns, p.vec = 8;
+    else if (ns == 16) p.n_slices = 8, p.vec = 16;
+    const size_t list_bytes = static_cast<size_t>(kWavesPerBlock) * g.n_tiles * g.capacity * 8;
+    const bool offsets_fit = static_cast<int64_t>(g.d_ff) * g.d_model * 2 < (int64_t{1} << 32);
+    if (p.n_slices > 0 && list_bytes <= 64 * 1024 && offsets_fit) {
+      const int64_t rows_per_xcd = (g.n_rows + (8 / p.n_slices) - 1) / (8 / p.n_slices);
+      const size_t split_bytes =
+          split_lists + static_cast<size_t>(P) * p.vec * kWave * 4;
+      if (g.n_rows * p.n_slices <= 1024 && split_bytes <= 64 * 1024) {
+        p.kind = SpmmKind::kSplitSliced;
+        p.blocks = static_cast<unsigned>(8 * rows_per_xcd);
+        p.lds_bytes = split_bytes;
+        return p;
+      }
+      const int64_t wg_per_xcd = (rows_per_xcd + kWavesPerBlock - 1) / kWavesPerBlock;
+      const int nslots = g.n_tiles * g.capacity;
+      const int spl = nslots % kWave == 0 ? nslots / kWave : 0;
+      p.kind = SpmmKind::kListSliced;
+      p.spl = (spl == 2 || spl == 4 || spl == 8) ? spl : 0;
+      p.blocks = static_cast<unsigned>(8 * (wg_per_xcd < 512 ? wg_per_xcd : 512));
+      p.lds_bytes = list_bytes;
+      return p;
+    }
+  }
+  const size_t split_bytes = split_lists + static_cast<size_t>(P) * V * kWave * 4;
+  if (g.n_rows * p.n_chunks <= 1024 && split_bytes <= 64 * 1024) {
+    p.kind = SpmmKind::kSplitChunk;
+    p.blocks = static_cast<unsigned>(g.n_rows);
+    p.lds_bytes = split_bytes;
+    return p;
+  }
+  const int64_t want = (g.n_rows * p.n_chunks + kWavesPerBlock - 1) / kWavesPerBlock;
+  p.kind = SpmmKind::kWaveChunk;
+  p.blocks = static_cast<unsigned>(want < 16384 ? want : 16384);
+  p.lds_bytes = 0;
+  return p;
+}
+
 }  // namespace
 
 bool spmm_split_plan(const Geometry& g, int waves, int parts_per_wave, SpmmSplitPlan* plan) {
-  // the conditions under which launch_spmm_sparse takes spmm_split_bf16_kernel
-  if (g.n_rows <= 0 || g.d_model % 512 != 0) return false;
-  const int ns = g.d_model / 512;
-  int n_slices = 0, vec = 0;
-  if (ns == 1 || ns == 2 || ns == 4 || ns == 8) n_slices = ns, vec = 8;
-  else if (ns == 16) n_slices = 8, vec = 16;
-  if (n_slices == 0) return false;
-  const size_t list_bytes = static_cast<size_t>(kWavesPerBlock) * g.n_tiles * g.capacity * 8;
-  const bool offsets_fit = static_cast<int64_t>(g.d_ff) * g.d_model * 2 < (int64_t{1} << 32);
-  if (list_bytes > 64 * 1024 || !offsets_fit || g.n_rows * n_slices > 1024) return false;
-  const int tpw = (g.n_tiles + waves * parts_per_wave - 1) / (waves * parts_per_wave);
-  plan->n_slices = n_slices;
-  plan->vec = vec;
-  plan->tpw = tpw;
-  plan->blocks = static_cast<unsigned>(8 * ((g.n_rows + (8 / n_slices) - 1) / (8 / n_slices)));
-  plan->lds_bytes = static_cast<size_t>(waves) * tpw * g.capacity * 8 +
-                    static_cast<size_t>(waves) * parts_per_wave * vec * kWave * 4;
-  return true;
+  if (g.n_rows <= 0) return false;
+  const SpmmPlan p = spmm_plan(g, 2);
+  if (p.kind != SpmmKind::kSplitSliced) return false;
+  // the same kSplitParts tile ranges, taken by `waves` waves of parts_per_wave each
+  plan->n_slices = p.n_slices;
+  plan->vec = p.vec;
+  plan->tpw = p.tpw;
+  plan->blocks = p.blocks;
+  plan->lds_bytes = static_cast<size_t>(waves) * p.tpw * g.capacity * 8 +
+                    static_cast<size_t>(waves) * parts_per_wave * p.vec * kWave * 4;
+  return waves * parts_per_wave == kSplitParts;
 }
 
 hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
                               const uint8_t* idx, const uint8_t* cnt, const int32_t* rows,
-                              const int32_t* n_rows_dev, const void* w_down, void* y,
-                              hipStream_t s) {
+                              const int32_t* n_rows_dev, const DenseSkip* skip_in,
+                              const void* w_down, void* y, hipStream_t s) {
   if (g.n_rows == 0) return hipSuccess;
-  const int V = elem_bytes == 2 ? 8 : 4;
-  const int n_chunks = (g.d_model + kWave * V - 1) / (kWave * V);
-  const int64_t items = g.n_rows * n_chunks;
-  const int64_t want = (items + kWavesPerBlock - 1) / kWavesPerBlock;
-  const unsigned blocks = static_cast<unsigned>(want < 16384 ? want : 16384);
+  const DenseSkip skip = (rows == nullptr && skip_in != nullptr) ? *skip_in
+                                                                  : DenseSkip{nullptr, nullptr, 0};
+  const SpmmPlan p = spmm_plan(g, elem_bytes);
+  constexpr int P = kSplitParts;
   if (elem_bytes == 2) {
-    // Column slices of 64 lanes x 8 bf16 (x 16 when d_model/8 needs it), one
-    // per XCD or shared by 2, 4, 8 XCDs; slot lists must fit in LDS.
-    int n_slices = 0, vec = 0;
-    if (g.d_model % 512 == 0) {
-      const int ns = g.d_model / 512;
-      if (ns == 1 || ns == 2 || ns == 4 || ns == 8) n_slices = ns, vec = 8;
-      else if (ns == 16) n_slices = 8, vec = 16;
-    }
-    const size_t list_bytes = static_cast<size_t>(kWavesPerBlock) * g.n_tiles * g.capacity * 8;
-    const bool offsets_fit = static_cast<int64_t>(g.d_ff) * g.d_model * 2 < (int64_t{1} << 32);
-    if (n_slices > 0 && list_bytes <= 64 * 1024 && offsets_fit) {
-      const int64_t rows_per_xcd = (g.n_rows + (8 / n_slices) - 1) / (8 / n_slices);
-      const int64_t wg_per_xcd = (rows_per_xcd + kWavesPerBlock - 1) / kWavesPerBlock;
-      const unsigned xblocks = static_cast<unsigned>(8 * (wg_per_xcd < 512 ? wg_per_xcd : 512));
-      const uint16_t* v16 = static_cast<const uint16_t*>(vals);
-      const uint16_t* w16 = static_cast<const uint16_t*>(w_down);
-      uint16_t* y16 = static_cast<uint16_t*>(y);
-      // Few rows: split each row over the 16 waves of a workgroup.
-      constexpr int P = kSplitParts;
-      const int tpw = (g.n_tiles + P - 1) / P;
-      const size_t split_bytes = static_cast<size_t>(P) * tpw * g.capacity * 8 +
-                                 static_cast<size_t>(P) * vec * kWave * 4;
-      if (g.n_rows * n_slices <= 1024 && split_bytes <= 64 * 1024) {
-        const int64_t rows_per_xcd = (g.n_rows + (8 / n_slices) - 1) / (8 / n_slices);
-        const unsigned sblocks = static_cast<unsigned>(8 * rows_per_xcd);
-        const uint16_t* v16 = static_cast<const uint16_t*>(vals);
-        const uint16_t* w16 = static_cast<const uint16_t*>(w_down);
-        uint16_t* y16 = static_cast<uint16_t*>(y);
-        if (vec == 8)
-          spmm_split_bf16_kernel<8, P><<<sblocks, P * kWave, split_bytes, s>>>(
-              v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity,
-              g.n_tiles, n_slices, tpw);
+    const uint16_t* v16 = static_cast<const uint16_t*>(vals);
+    const uint16_t* w16 = static_cast<const uint16_t*>(w_down);
+    uint16_t* y16 = static_cast<uint16_t*>(y);
+    switch (p.kind) {
+      case SpmmKind::kSplitSliced:
+        if (p.vec == 8)
+          spmm_split_bf16_kernel<8, P><<<p.blocks, P * kWave, p.lds_bytes, s>>>(
+              v16, idx, cnt, rows, n_rows_dev, skip, w16, y16, g.n_rows, g.d_model, g.tile,
+              g.capacity, g.n_tiles, p.n_slices, p.tpw);
         else
-          spmm_split_bf16_kernel<16, P><<<sblocks, P * kWave, split_bytes, s>>>(
-              v16, idx, cnt, rows, n_rows_dev, w16, y16, g.n_rows, g.d_model, g.tile, g.capacity,
-              g.n_tiles, n_slices, tpw);
-        return hipGetLastError();
+          spmm_split_bf16_kernel<16, P><<<p.blocks, P * kWave, p.lds_bytes, s>>>(
+              v16, idx, cnt, rows, n_rows_dev, skip, w16, y16, g.n_rows, g.d_model, g.tile,
+              g.capacity, g.n_tiles, p.n_slices, p.tpw);
+        break;
+      case SpmmKind::kListSliced: {
+        auto go = [&](auto vc, auto sc) {
+          spmm_list_bf16_kernel<decltype(vc)::value, decltype(sc)::value>
+              <<<p.blocks, kThreads, p.lds_bytes, s>>>(v16, idx, cnt, rows, n_rows_dev, skip, w16,
+                                                       y16, g.n_rows, g.d_model, g.tile,
+                                                       g.capacity, g.n_tiles, p.n_slices);
+        };
+        auto by_spl = [&](auto vc) {
+          if (p.spl == 2) go(vc, std::integral_constant<int, 2>{});
+          else if (p.spl == 4) go(vc, std::integral_constant<int, 4>{});
+          else if (p.spl == 8) go(vc, std::integral_constant<int, 8>{});
+          else go(vc, std::integral_constant<int, 0>{});
+        };
+        if (p.vec == 8) by_spl(std::integral_constant<int, 8>{});
+        else by_spl(std::integral_constant<int, 16>{});
+        break;
       }
-      // slots per lane when a row's slots fill whole waves (4 at the 1B layer)
-      const int nslots = g.n_tiles * g.capacity;
-      const int spl = nslots % kWave == 0 ? nslots / kWave : 0;
-      auto go = [&](auto vc, auto sc) {
-        spmm_list_bf16_kernel<decltype(vc)::value, decltype(sc)::value>
-            <<<xblocks, kThreads, list_bytes, s>>>(v16, idx, cnt, rows, n_rows_dev, w16, y16,
-                                                   g.n_rows, g.d_model, g.tile, g.capacity,
-                                                   g.n_tiles, n_slices);
-      };
-      auto by_spl = [&](auto vc) {
-        if (spl == 2) go(vc, std::integral_constant<int, 2>{});
-        else if (spl == 4) go(vc, std::integral_constant<int, 4>{});
-        else if (spl == 8) go(vc, std::integral_constant<int, 8>{});
-        else go(vc, std::integral_constant<int, 0>{});
-      };
-      if (vec == 8) by_spl(std::integral_constant<int, 8>{});
-      else by_spl(std::integral_constant<int, 16>{});
-      return hipGetLastError();
+      case SpmmKind::kSplitChunk:
+        spmm_split_kernel<uint16_t, P><<<dim3(p.blocks, p.n_chunks), P * kWave, p.lds_bytes, s>>>(
+            v16, idx, cnt, rows, n_rows_dev, skip, w16, y16, g.n_rows, g.d_model, g.tile,
+            g.capacity, g.n_tiles, p.n_chunks, p.tpw);
+        break;
+      case SpmmKind::kWaveChunk:
+        spmm_sparse_kernel<uint16_t><<<p.blocks, kThreads, 0, s>>>(
+            v16, idx, cnt, rows, n_rows_dev, skip, w16, y16, g.n_rows, g.d_model, g.tile,
+            g.capacity, g.n_tiles, p.n_chunks);
+        break;
     }
-    {  // few rows, d_model the sliced kernel does not take: split each row over 16 waves
-      constexpr int P = 16;
-      const int tpw = (g.n_tiles + P - 1) / P;
-      const size_t split_bytes = static_cast<size_t>(P) * tpw * g.capacity * 8 +
-                                 static_cast<size_t>(P) * SpmmVec<uint16_t>::N * kWave * 4;
-      if (g.n_rows * n_chunks <= 1024 && split_bytes <= 64 * 1024) {
-        spmm_split_kernel<uint16_t, P><<<dim3(static_cast<unsigned>(g.n_rows), n_chunks),
-                                         P * kWave, split_bytes, s>>>(
-            static_cast<const uint16_t*>(vals), idx, cnt, rows, n_rows_dev,
-            static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y), g.n_rows, g.d_model,
-            g.tile, g.capacity, g.n_tiles, n_chunks, tpw);
-        return hipGetLastError();
-      }
-    }
-    spmm_sparse_kernel<uint16_t><<<blocks, kThreads, 0, s>>>(
-        static_cast<const uint16_t*>(vals), idx, cnt, rows, n_rows_dev, static_cast<const uint16_t*>(w_down),
-        static_cast<uint16_t*>(y), g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles, n_chunks);
   } else {
-    // Few rows: split each row over the 16 waves of a workgroup.
-    constexpr int P = 16;
-    const int tpw = (g.n_tiles + P - 1) / P;
-    const size_t split_bytes = static_cast<size_t>(P) * tpw * g.capacity * 8 +
-                               static_cast<size_t>(P) * SpmmVec<float>::N * kWave * 4;
-    if (g.n_rows * n_chunks <= 1024 && split_bytes <= 64 * 1024) {
-      spmm_split_kernel<float, P><<<dim3(static_cast<unsigned>(g.n_rows), n_chunks), P * kWave,
-                                    split_bytes, s>>>(
-          static_cast<const float*>(vals), idx, cnt, rows, n_rows_dev,
-          static_cast<const float*>(w_down), static_cast<float*>(y), g.n_rows, g.d_model, g.tile,
-          g.capacity, g.n_tiles, n_chunks, tpw);
-      return hipGetLastError();
-    }
-    spmm_sparse_kernel<float><<<blocks, kThreads, 0, s>>>(
-        static_cast<const float*>(vals), idx, cnt, rows, n_rows_dev, static_cast<const float*>(w_down),
-        static_cast<float*>(y), g.n_rows, g.d_model, g.tile, g.capacity, g.n_tiles, n_chunks);
+    const float* v32 = static_cast<const float*>(vals);
+    const float* w32 = static_cast<const float*>(w_down);
+    float* y32 = static_cast<float*>(y);
+    if (p.kind == SpmmKind::kSplitChunk)
+      spmm_split_kernel<float, P><<<dim3(p.blocks, p.n_chunks), P * kWave, p.lds_bytes, s>>>(
+          v32, idx, cnt, rows, n_rows_dev, skip, w32, y32, g.n_rows, g.d_model, g.tile,
+          g.capacity, g.n_tiles, p.n_chunks, p.tpw);
+    else
+      spmm_sparse_kernel<float><<<p.blocks, kThreads, 0, s>>>(
+          v32, idx, cnt, rows, n_rows_dev, skip, w32, y32, g.n_rows, g.d_model, g.tile,
+          g.capacity, g.n_tiles, p.n_chunks);
   }
   return hipGetLastError();
 }

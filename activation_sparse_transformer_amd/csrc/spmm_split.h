@@ -6,6 +6,7 @@
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace twell {
 namespace {
@@ -80,7 +81,7 @@ __device__ __forceinline__ void spmm_split_rows(
     const uint8_t* __restrict__ cnt, const int32_t* __restrict__ rows,
     const int32_t* __restrict__ n_rows_dev, const uint16_t* __restrict__ w,
     uint16_t* __restrict__ y, int64_t N, int dm, int T, int C, int nt, int n_slices, int tpw,
-    uint2* lists, int64_t vblock, int64_t vgrid) {
+    uint2* lists, int64_t vblock, int64_t vgrid, DenseSkip skip = DenseSkip{nullptr, nullptr, 0}) {
   constexpr int PV = P * V;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int wslots = tpw * C;
@@ -96,6 +97,7 @@ __device__ __forceinline__ void spmm_split_rows(
   const int64_t R = rows != nullptr ? min(static_cast<int64_t>(*n_rows_dev), N) : N;
   for (int64_t k = part + parts * (vblock / 8); k < R; k += parts * per_xcd) {
     const int64_t n = rows != nullptr ? rows[k] : k;
+    if (rows == nullptr && listed_dense(n, skip.dense_rows, skip.n_dense, skip.cap)) continue;
     const int64_t s0 = n * nt * C;
     for (int vv = 0; vv < V; ++vv) {
       const int pv = wave * V + vv;

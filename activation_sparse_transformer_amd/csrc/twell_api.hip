@@ -4,8 +4,6 @@
 #include "../../include/twell.h"
 #include "kernels.h"
 
-#include <mutex>
-
 #define TWELL_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace twell {
@@ -103,39 +101,6 @@ PackWorkspace carve(const twell_shape* s, void* ws, bool with_spill) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_ERR_HIP; }
-
-// Per-device auxiliary stream on which the forward pass runs its sparse
-// product while the dense fallback runs on the caller's stream (the two
-// write disjoint rows of y).  Created on first use, default priority,
-// non-blocking; it and its two events live until the process ends.  The
-// mutex serialises the fork / join enqueue of concurrent host threads.
-struct AuxStream {
-  std::once_flag once;
-  hipError_t err = hipSuccess;
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  std::mutex mu;
-};
-constexpr int kMaxDevices = 64;
-AuxStream g_aux[kMaxDevices];
-
-AuxStream* aux_stream(hipError_t* err) {
-  int dev = 0;
-  *err = hipGetDevice(&dev);
-  if (*err != hipSuccess) return nullptr;
-  if (dev < 0 || dev >= kMaxDevices) {
-    *err = hipErrorInvalidDevice;
-    return nullptr;
-  }
-  AuxStream* a = &g_aux[dev];
-  std::call_once(a->once, [a] {
-    a->err = hipStreamCreateWithFlags(&a->stream, hipStreamNonBlocking);
-    if (a->err == hipSuccess) a->err = hipEventCreateWithFlags(&a->fork, hipEventDisableTiming);
-    if (a->err == hipSuccess) a->err = hipEventCreateWithFlags(&a->join, hipEventDisableTiming);
-  });
-  *err = a->err;
-  return a->err == hipSuccess ? a : nullptr;
-}
 
 #define TWELL_TRY(expr)                          \
   do {                                           \
@@ -248,24 +213,9 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
     return rc;
   TWELL_TRY(mark(2));
   // 3. sparse down-projection of the TwELL rows and 4. dense fallback for the
-  // dense rows.  They write disjoint rows of y: the plain call runs 3 on the
-  // auxiliary stream concurrently with 4 on the caller's stream when the batch
-  // has more than 64 rows; with fewer the fork and join cost more than the
-  // overlap gives (measured: 83 against 89 us at 16 rows), and the timed
-  // variant runs them one after the other so each stage can be timed alone.
+  // dense rows, one after the other on the caller's stream (they write
+  // disjoint rows of y).
   if (g.n_rows > 0) {
-    AuxStream* a = nullptr;
-    std::unique_lock<std::mutex> lock;
-    hipStream_t sp = st;
-    if (ev == nullptr && g.n_rows > kSkinnyMaxRows) {
-      hipError_t e = hipSuccess;
-      a = aux_stream(&e);
-      TWELL_TRY(e);
-      lock = std::unique_lock<std::mutex>(a->mu);
-      TWELL_TRY(hipEventRecord(a->fork, st));
-      TWELL_TRY(hipStreamWaitEvent(a->stream, a->fork, 0));
-      sp = a->stream;
-    }
     // batches of at most 64 bf16 rows (plain call): the sparse product runs as
     // extra workgroups of the fallback's split-K launch, inside its weight stream
     const bool merged = ev == nullptr && eb == 2 && w.skinny != nullptr && fallback_takes_spmm(g);
@@ -278,7 +228,7 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
           st, w.skinny, sr));
     } else if (!build_spmm) {
       TWELL_TRY(launch_spmm_sparse(g, eb, h_out->values, h_out->indices, h_out->counts,
-                                   w.route.sparse_rows, w.route.n_sparse, w_down, y, sp));
+                                   w.route.sparse_rows, w.route.n_sparse, nullptr, w_down, y, st));
     }
     TWELL_TRY(mark(3));
     if (merged) {
@@ -293,10 +243,6 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
                                     h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
                                     static_cast<const float*>(w_down), static_cast<float*>(y),
                                     st, w.skinny));
-    if (a != nullptr) {
-      TWELL_TRY(hipEventRecord(a->join, a->stream));
-      TWELL_TRY(hipStreamWaitEvent(st, a->join, 0));
-    }
   } else {
     TWELL_TRY(mark(3));
   }
@@ -369,10 +315,11 @@ TWELL_EXPORT int twell_spmm(const twell_shape* shape, const twell_hybrid* in, co
   if (g.n_rows == 0) return TWELL_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int eb = elem_bytes(shape->dtype);
-  // every row from its TwELL slots (dense rows hold none and come out 0) ...
+  // the TwELL rows (a row listed among the stored dense rows is skipped) ...
+  const DenseSkip skip{in->dense_rows, in->n_dense, in->dense_capacity};
   TWELL_TRY(launch_spmm_sparse(g, eb, in->values, in->indices, in->counts, nullptr, nullptr,
-                               w_down, y, st));
-  // ... then the stored dense rows are overwritten by the fallback GEMM
+                               in->dense_capacity > 0 ? &skip : nullptr, w_down, y, st));
+  // ... and the stored dense rows by the dense fallback GEMM
   if (eb == 2)
     TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(in->dense_values),
                                    in->dense_rows, in->n_dense, in->dense_capacity,

@@ -11,11 +11,13 @@ layer); reading rather than writing it leaves clean lines, so the timed
 kernels pay no write-backs of the eviction's data.  Each stage is timed with HIP events recorded by the library on the
 stream its kernels run on.
 
-Prints ONE JSON line.  Besides the throughput it carries the roofline of the
-dominant kernel, the sparse down-projection's roofline against HBM, the same
-layer as a plain dense bf16 FFN through torch (hipBLASLt), the 16-token decode
-layer against its dense FFN ("secondary"), and the CPU oracle timed on a
-bounded sample of rows on this host's cores.
+Every time reported is the median over the timed steps (p10 and p90 beside
+it).  Prints ONE JSON line.  Besides the throughput it carries the roofline
+of the dominant kernel, the sparse down-projection's roofline against HBM,
+the same layer as a plain dense bf16 FFN through torch (hipBLASLt), every
+other workload's forward against its own dense FFN ("layers"), the
+conversions, and the CPU oracle timed on a bounded sample of rows on this
+host's cores.
 """
 from __future__ import annotations
 
@@ -73,6 +75,10 @@ def percentile(a, q):
     return float(np.percentile(np.asarray(a), q))
 
 
+def median(a):
+    return float(np.median(np.asarray(a)))
+
+
 def flush_cache(buf: torch.Tensor, k: int) -> None:
     """Evicts the weights from L2 and the 256 MB Infinity Cache before a step.
 
@@ -84,15 +90,14 @@ def flush_cache(buf: torch.Tensor, k: int) -> None:
     buf.view(torch.int64).max()
 
 
-def time_forward(cfg, d, bufs, steps, warmup, flush):
+def time_forward(cfg, d, bufs, steps, warmup, flush, stages=True):
     """ffn_sparse_forward, cold cache.
 
     Two timed loops of `steps` each: the headline times whole plain calls with
-    an event pair around each (the sparse product then runs on the library's
-    auxiliary stream, concurrently with the dense fallback); the breakdown uses
-    ffn_sparse_forward_events, which runs the four stages one after the other
-    with events between them, so each stage is one kernel sequence timed
-    alone and its total is not the headline.
+    an event pair around each; the breakdown uses ffn_sparse_forward_events,
+    which runs each of the four stages in its own launches with events between
+    them, so each stage is one kernel sequence timed alone and its total is
+    not the headline.
     """
     fwd = lambda **kw: twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"],
                                                 cfg.tile, cfg.capacity, out=bufs, **kw)
@@ -111,6 +116,8 @@ def time_forward(cfg, d, bufs, steps, warmup, flush):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total = [a.elapsed_time(b) for a, b in pairs]
+    if not stages:
+        return total, None, None, wall
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     for i in range(steps):
         flush_cache(flush, i)
@@ -165,29 +172,33 @@ def time_dense(d, steps, warmup, flush):
     return [a.elapsed_time(b) for a, b in ts]
 
 
-# A second layer timed in the same run beside the headline one: the 16-token
-# decode layer, where the whole weight pair is streamed once either way and the
-# sparse path has the most to skip.  Reported under "secondary", never as value.
-SECONDARY_WORKLOAD = "decode_bf16"
-
-
-def time_secondary(cfg, steps, warmup, flush, dev):
-    """Plain-call forward and the dense torch FFN of another layer, cold cache."""
-    t = make_inputs(cfg)
+# Every other workload is timed in the same run beside the headline one, its
+# forward (plain calls) against its own dense torch FFN, with the same timing
+# method.  Reported under "layers", never as value.
+def time_layer(cfg, steps, warmup, flush, dev, t=None):
+    """Plain-call forward and the dense torch FFN of one layer, cold cache."""
+    t = make_inputs(cfg) if t is None else t
     d = {k: v.to(dev) for k, v in t.items()}
     bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
                                  cfg.torch_dtype, dev)
-    total, _, _, _ = time_forward(cfg, d, bufs, steps, warmup, flush)
+    total, _, _, _ = time_forward(cfg, d, bufs, steps, warmup, flush, stages=False)
     if int(bufs.status.item()) != twell.TWELL_OK:
-        raise RuntimeError("secondary forward reported an error status")
+        raise RuntimeError(f"{cfg.name} forward reported an error status")
+    n_dense = bufs.hybrid.n_dense_host()
+    del bufs
+    torch.cuda.empty_cache()
     dense = time_dense(d, steps, warmup, flush)
-    ms, dms = float(np.mean(total)), float(np.mean(dense))
+    ms, dms = median(total), median(dense)
     out = {"workload": cfg.name, "n_rows": cfg.n_rows, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
-           "tile": cfg.tile, "capacity": cfg.capacity, "dtype": cfg.dtype,
-           "n_dense": bufs.hybrid.n_dense_host(),
-           "ms_per_step": ms, "tokens_per_s": cfg.n_rows / (ms * 1e-3),
-           "dense_ffn_ms": dms, "speedup_twell_over_dense": dms / ms}
-    del d, bufs
+           "tile": cfg.tile, "capacity": cfg.capacity, "dtype": cfg.dtype, "steps": steps,
+           "n_dense": n_dense,
+           "ms_per_step": ms, "ms_p10": percentile(total, 10), "ms_p90": percentile(total, 90),
+           "tokens_per_s": cfg.n_rows / (ms * 1e-3),
+           "effective_tflops": 4.0 * cfg.n_rows * cfg.d_model * cfg.d_ff / (ms * 1e-3) / 1e12,
+           "dense_ffn_ms": dms, "dense_ffn_p10": percentile(dense, 10),
+           "dense_ffn_p90": percentile(dense, 90),
+           "speedup_twell_over_dense": dms / ms}
+    del d
     torch.cuda.empty_cache()
     return out
 
@@ -230,9 +241,9 @@ def conversion_bytes(n_rows, d_ff, tile, capacity, elem_bytes, n_dense):
     return n_rows * d_ff * elem_bytes + twell_bytes + n_dense * d_ff * elem_bytes
 
 
-def time_conversions(cfg, steps, warmup, flush, dev):
+def time_conversions(cfg, steps, warmup, flush, dev, t=None):
     """twell_pack and twell_unpack on an h of the layer, cold cache."""
-    t = make_inputs(cfg)
+    t = make_inputs(cfg) if t is None else t
     x, w_up_t = t["x"].to(dev), t["w_up_t"].to(dev)
     b16 = t["b_up"].to(dev).to(cfg.torch_dtype)
     del t
@@ -260,7 +271,7 @@ def time_conversions(cfg, steps, warmup, flush, dev):
     nbytes = conversion_bytes(cfg.n_rows, cfg.d_ff, cfg.tile, cfg.capacity, e, n_dense)
 
     def stage(ms_list, kernels):
-        ms = float(np.mean(ms_list))
+        ms = median(ms_list)
         gbs = nbytes / (ms * 1e-3) / 1e9
         return {"ms": ms, "ms_p10": percentile(ms_list, 10), "ms_p90": percentile(ms_list, 90),
                 "bound": "hbm", "bytes_per_launch": nbytes, "achieved": gbs, "unit": "GB/s",
@@ -328,19 +339,37 @@ def hybrid_stats(cfg, bufs):
     return n_dense, nnz_sparse, n_unique
 
 
+def blas_info():
+    """The BLAS NumPy was built against (numpy.show_config) and the one loaded."""
+    out = {}
+    try:
+        dep = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        out["build"] = f"{dep.get('name')} {dep.get('version')}"
+    except Exception:  # pragma: no cover
+        out["build"] = None
+    try:
+        from threadpoolctl import threadpool_info
+        out["loaded"] = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info()
+                         if p.get("user_api") == "blas"]
+    except Exception:  # pragma: no cover
+        out["loaded"] = None
+    return out
+
+
 def cpu_oracle_baseline(t, cfg, target_s=20.0):
-    """The CPU oracle (float64 dense FFN) on a bounded, seeded sample of rows.
+    """The CPU oracle (float64 dense FFN) on a bounded, seeded sample of rows,
+    with the BLAS threads set to the cores this process may run on.
 
     The per-row cost is calibrated on 256 rows; whole passes usually run
     faster per row than that, so a 20 s target lands at about 10-20 s."""
     import oracle  # test infrastructure: only this leg of the benchmark uses it
 
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"), default=1)
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores, user_api="blas")
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        limiter = None
     x = t["x"].double().numpy()
     w_up_t = t["w_up_t"].double().numpy()
     b = t["b_up"].double().numpy()
@@ -359,26 +388,31 @@ def cpu_oracle_baseline(t, cfg, target_s=20.0):
     for _ in range(reps):
         oracle.ffn_forward_rows(x, w_up_t, b, w_down, rows[:n_rows])
     el = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.restore_original_limits()
     n_rows_total = n_rows * reps
     return {
-        "value": n_rows_total / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+        "value": n_rows_total / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "blas": blas_info(),
         "sample": f"{n_rows} of {cfg.n_rows} token rows (seeded permutation) x {reps} pass(es), "
-                  f"float64 dense FFN in NumPy, {el:.1f} s",
+                  f"float64 dense FFN in NumPy, BLAS threads = cores = {cores}, {el:.1f} s",
     }
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layer-steps", type=int, default=20,
+                    help="timed steps for each other workload (the 16384-token one takes 5)")
     ap.add_argument("--workload", default="ffn_1b_bf16", choices=sorted(CONFIGS))
     ap.add_argument("--capacity", type=int, default=None,
                     help="slots per tile instead of the workload's own (same inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the second (decode-sized) layer timed beside the headline one")
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the other workloads timed beside the headline one")
     ap.add_argument("--no-conversions", action="store_true",
                     help="skip twell_pack / twell_unpack on the 16384-token layer's h")
     args = ap.parse_args(argv)
@@ -412,7 +446,7 @@ def main(argv=None):
     status = int(bufs.status.item())
     if status != twell.TWELL_OK:
         raise RuntimeError(f"forward reported {twell.status_string(status)}")
-    ms = float(np.mean(total))
+    ms = median(total)
     warm = time_forward_warm(cfg, d, bufs, args.steps)
     n_dense, nnz_sparse, n_unique = hybrid_stats(cfg, bufs)
     e = cfg.elem_bytes
@@ -425,7 +459,7 @@ def main(argv=None):
     spmm_flops = 2.0 * nnz_sparse * dm
     fb_flops = 2.0 * n_dense * dff * dm
     route_bytes = (N * nt + 4 * N + n_dense * dff * e * 2 + n_dense * nt * (C * e + C + 1))
-    stage_ms = {s: float(np.mean(v)) for s, v in per_stage.items()}
+    stage_ms = {s: median(v) for s, v in per_stage.items()}
     stages = {
         "up_gemm_pack": {"ms": stage_ms["up_gemm_pack"], "bound": "mfma", "unit": "TFLOP/s",
                          "achieved": up_flops / (stage_ms["up_gemm_pack"] * 1e-3) / 1e12,
@@ -481,14 +515,15 @@ def main(argv=None):
         "ms_per_step_p10": percentile(total, 10),
         "ms_per_step_p90": percentile(total, 90),
         "wall_s_timed_loop": wall,
-        "ms_per_step_with_stage_events": float(np.mean(staged_total)),
+        "ms_per_step_with_stage_events": median(staged_total),
+        "timing": f"median of {args.steps} cold-cache steps after {args.warmup} warm-up steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
         "cache": "cold (1 GiB read between steps)",
-        "warm_cache_ms_per_step": float(np.mean(warm)),
+        "warm_cache_ms_per_step": median(warm),
         "config": {
             "workload": cfg.name, "n_rows": N, "d_model": dm, "d_ff": dff, "tile": cfg.tile,
             "capacity": C, "b0": cfg.b0, "seed": cfg.seed,
@@ -506,29 +541,37 @@ def main(argv=None):
     if not args.no_dense_baseline:
         log("[bench] dense bf16 FFN through torch")
         dense = time_dense(d, args.steps, args.warmup, flush)
-        dms = float(np.mean(dense))
+        dms = median(dense)
         result["dense_bf16_ffn"] = {
-            "ms": dms, "tokens_per_s": N / (dms * 1e-3),
+            "ms": dms, "ms_p10": percentile(dense, 10), "ms_p90": percentile(dense, 90),
+            "tokens_per_s": N / (dms * 1e-3),
             "tflops": 4.0 * N * dm * dff / (dms * 1e-3) / 1e12,
             "mfma_frac": 4.0 * N * dm * dff / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "speedup_twell_over_dense": dms / ms,
         }
-    if not args.no_secondary and cfg.name != SECONDARY_WORKLOAD:
-        log(f"[bench] secondary workload {SECONDARY_WORKLOAD}")
+    if "d" in locals():
         del d, bufs
-        torch.cuda.empty_cache()
-        result["secondary"] = time_secondary(CONFIGS[SECONDARY_WORKLOAD], args.steps, args.warmup,
-                                             flush, dev)
-        # the 64-token fp32 parity layer: per-call time, launch latency dominated
-        result["secondary_tiny"] = time_secondary(CONFIGS["tiny_fp32"], args.steps, args.warmup,
-                                                  flush, dev)
+    torch.cuda.empty_cache()
+    large_inputs = None
+    if not args.no_layers:
+        result["layers"] = {}
+        for name in CONFIGS:
+            if name == cfg.name:
+                continue
+            lc = CONFIGS[name]
+            big = lc.n_rows * lc.d_ff >= (1 << 28)
+            steps = max(3, args.layer_steps // 4) if big else args.layer_steps
+            log(f"[bench] layer {name}: {steps} steps")
+            lt = make_inputs(lc)
+            if name == CONVERSION_WORKLOAD:
+                large_inputs = lt
+            result["layers"][name] = time_layer(lc, steps, min(args.warmup, 3), flush, dev, lt)
+            del lt
     if not args.no_conversions:
         log(f"[bench] conversions on {CONVERSION_WORKLOAD}")
-        if "d" in locals():
-            del d, bufs
-        torch.cuda.empty_cache()
         result["conversions"] = time_conversions(CONFIGS[CONVERSION_WORKLOAD], args.steps,
-                                                 args.warmup, flush, dev)
+                                                 args.warmup, flush, dev, large_inputs)
+    del large_inputs
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle on a sample of rows")
         result["cpu_baseline"] = cpu_oracle_baseline(t, cfg)

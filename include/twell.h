@@ -82,7 +82,10 @@ typedef enum twell_status {
 
 typedef enum twell_dtype { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
 
-/* Shape of one FFN layer and its TwELL geometry.
+/* Shape of one FFN layer and its TwELL geometry (tile width T and capacity
+ * C of "Sparser, Faster, Lighter Transformer Language Models (Sakana AI +
+ * NVIDIA)", Figure 1 description; the configuration names T and C, the pages
+ * name T and the tile index t).
  * Requirements: n_rows >= 0 and < 2^31; d_model > 0 and a multiple of 8;
  * d_ff > 0 and a multiple of tile; tile in {64, 128, 256} (other tile widths
  * are TWELL_ERR_UNSUPPORTED); 1 <= capacity <= min(tile, 255); dtype a
@@ -97,7 +100,10 @@ typedef struct twell_shape {
   int32_t reserved; /* must be 0 */
 } twell_shape;
 
-/* A hybrid TwELL matrix [n_rows][d_ff] (all device pointers, caller-owned).
+/* A hybrid TwELL matrix [n_rows][d_ff] (all device pointers, caller-owned):
+ * the values / tile-local indices / per-tile counts of "Sparser, Faster,
+ * Lighter Transformer Language Models (Sakana AI + NVIDIA)", Figure 1
+ * description (panel b), plus the dense rows of its hybrid split (panel c).
  *  values       [n_rows][nt][capacity]   dtype
  *  indices      [n_rows][nt][capacity]   uint8, tile-local column
  *  counts       [n_rows][nt]             uint8
@@ -117,19 +123,33 @@ typedef struct twell_hybrid {
   int64_t dense_capacity;
 } twell_hybrid;
 
-/* Library version (TWELL_VERSION). */
+/* Library version (TWELL_VERSION).  Defined by this interface, not by the
+ * pages. */
 int twell_version(void);
 
-/* Static string naming a twell_status value ("unknown status" otherwise). */
+/* Static string naming a twell_status value ("unknown status" otherwise).
+ * Defined by this interface, not by the pages. */
 const char* twell_status_string(int status);
 
 /* Bytes of device workspace ffn_sparse_forward needs for this shape
  * (0 for an invalid shape).  Sized for the worst case: every tile spilled;
- * batches of at most 64 rows add room for fp32 split-K partial sums. */
+ * batches of at most 64 rows add room for fp32 split-K partial sums.
+ * The scratch behind the fused pass of "SakanaAI/sparser-faster-llms: How
+ * TwELL Makes Sparse Transformers Run Like They Were Built for Hopper",
+ * section "TwELL: The Packing Format That Fits the Machine". */
 size_t ffn_sparse_workspace_size(const twell_shape* shape);
 
 /* The fused forward pass: y = ReLU(x W_up + b_up) W_down, with the hidden
  * activations h produced directly in hybrid TwELL form.
+ * Defined by: "SakanaAI/sparser-faster-llms: How TwELL Makes Sparse
+ * Transformers Run Like They Were Built for Hopper", section "TwELL: The
+ * Packing Format That Fits the Machine" (fused MLP execution that packs the
+ * up-projection's output without a separate pass over memory); "Nvidia and
+ * Sakana make LLMs 30% faster by doing less math", section "Reshaping math
+ * for the GPU" (sparse tokens on the fast path, rare dense tokens through a
+ * dense matrix); "The Relentless Search for Efficiency in Large-Scale
+ * Language Models", section "Mechanism of Action: Kernel-Level Optimization"
+ * (the down-projection reads only the rows of active units).
  *   1. up-projection GEMM (MFMA for bf16) + bias + ReLU + rounding, whose
  *      epilogue packs each (row, tile) of h into TwELL and flags overflow
  *      (at most 64 rows: K is split over workgroups whose fp32 partial sums
@@ -142,15 +162,10 @@ size_t ffn_sparse_workspace_size(const twell_shape* shape);
  *      of value * w_down[t*tile + index];
  *   4. dense fallback GEMM for the dense rows: y[dense_rows[m]] =
  *      dense_values[m] W_down.
- * Steps 3 and 4 write disjoint rows of y.  For more than 64 rows they run
- * concurrently: step 3 on a library-owned auxiliary stream of the current
- * device (created on the first such call, kept until the process ends),
- * forked from and joined back into `stream` with events, so all work still
- * completes in `stream` order and the pass can be captured into a HIP graph
- * from `stream`.  Calls on one device share that auxiliary stream.  For at
- * most 64 rows both run in order on `stream`; step 3 may then share a launch with
- * step 4 (bf16) or with step 2's dense-row build (float32, rows of at most
- * 64 KB, when the shape allows), computing the same bits as when it runs alone.
+ * Steps 3 and 4 write disjoint rows of y and run one after the other on
+ * `stream`.  For at most 64 rows step 3 may share a launch with step 4 (bf16)
+ * or with step 2's dense-row build (float32, rows of at most 64 KB, when the
+ * shape allows), computing the same bits as when it runs alone.
  * Arguments: shape (host pointer); x, w_up_t, b_up, w_down inputs; y output;
  * h_out (host pointer to a struct of device pointers) receives h in hybrid
  * TwELL form; h_dense_debug, if non-NULL, receives h [n_rows][d_ff] exactly
@@ -169,23 +184,33 @@ int ffn_sparse_forward(const twell_shape* shape, const void* x, const void* w_up
 
 /* ffn_sparse_forward that also records five caller-created HIP events
  * (stage_events[0..4], hipEvent_t passed as void*) on `stream`: before step
- * 1 and after each of steps 1-4.  Here steps 3 and 4 run one after the other
- * on `stream` (no auxiliary stream), so a caller can time every stage alone
- * with hipEventElapsedTime on the stream the kernels run on.  Same arguments,
- * results and errors as ffn_sparse_forward; a NULL array or event is
- * TWELL_ERR_INVALID_ARG. */
+ * 1 and after each of steps 1-4.  Every stage here runs in its own launches
+ * (no step shares a launch with another), so a caller can time each stage
+ * alone with hipEventElapsedTime.  Same arguments, results and errors as
+ * ffn_sparse_forward; a NULL array or event is TWELL_ERR_INVALID_ARG.
+ * Defined by the same passages as ffn_sparse_forward; the events are this
+ * interface's own, for measurement. */
 int ffn_sparse_forward_events(const twell_shape* shape, const void* x, const void* w_up_t,
                               const float* b_up, const void* w_down, void* y,
                               const twell_hybrid* h_out, void* h_dense_debug, void* workspace,
                               size_t workspace_bytes, int32_t* d_status, void* stream,
                               void* const* stage_events);
 
-/* Bytes of device workspace twell_pack needs (0 for an invalid shape). */
+/* Bytes of device workspace twell_pack needs (0 for an invalid shape):
+ * per-(row, tile) overflow flags and the row routing lists.  The scratch
+ * behind dense_to_twell of "SakanaAI/sparser-faster-llms: How TwELL Makes
+ * Sparse Transformers Run Like They Were Built for Hopper", section "TwELL:
+ * The Packing Format That Fits the Machine". */
 size_t twell_pack_workspace_size(const twell_shape* shape);
 
 /* dense_to_twell: pack h [n_rows][d_ff] into the hybrid `out` under the
  * format rules above (same rules and same result as step 1-2 of
- * ffn_sparse_forward applied to h).  Dense rows are copied bit for bit; in
+ * ffn_sparse_forward applied to h).
+ * Defined by: "SakanaAI/sparser-faster-llms: How TwELL Makes Sparse
+ * Transformers Run Like They Were Built for Hopper", section "TwELL: The
+ * Packing Format That Fits the Machine" (the dense-to-TwELL path); format and
+ * row split per "Sparser, Faster, Lighter Transformer Language Models (Sakana
+ * AI + NVIDIA)", Figure 1 description and packing-format flowchart.  Dense rows are copied bit for bit; in
  * sparse rows a -0.0 is dropped like +0.0.  workspace / d_status as for
  * ffn_sparse_forward. */
 int twell_pack(const twell_shape* shape, const void* h, const twell_hybrid* out,
@@ -194,12 +219,26 @@ int twell_pack(const twell_shape* shape, const void* h, const twell_hybrid* out,
 /* twell_to_dense: h [n_rows][d_ff] = +0.0 everywhere, then every stored slot
  * (k < counts) is written to its column and every stored dense row
  * (the first min(*n_dense, dense_capacity) entries) is copied to its row.
- * dense_rows must be strictly ascending. */
+ * dense_rows must be strictly ascending.
+ * Defined by: "SakanaAI/sparser-faster-llms: How TwELL Makes Sparse
+ * Transformers Run Like They Were Built for Hopper", section "TwELL: The
+ * Packing Format That Fits the Machine" (the TwELL-to-dense path); format per
+ * "Sparser, Faster, Lighter Transformer Language Models (Sakana AI +
+ * NVIDIA)", Figure 1 description. */
 int twell_unpack(const twell_shape* shape, const twell_hybrid* in, void* h, void* stream);
 
 /* The hybrid down-projection y [n_rows][d_model] = unpack(in) W_down:
  * TwELL rows by the sparse gather kernel, stored dense rows by the dense
- * fallback GEMM (float32 accumulation, one rounding at the end). */
+ * fallback GEMM (float32 accumulation, one rounding at the end).  Every row
+ * of y is written once: a row listed among the stored dense rows
+ * (dense_rows[0 .. min(*n_dense, dense_capacity)), strictly ascending) by the
+ * fallback only, every other row by the sparse kernel from its slots (a row
+ * with no stored slot gets +0.0).
+ * Defined by: "The Relentless Search for Efficiency in Large-Scale Language
+ * Models", section "Mechanism of Action: Kernel-Level Optimization" (only the
+ * weight rows of non-zero activations are read); "Nvidia and Sakana make
+ * LLMs 30% faster by doing less math", section "Reshaping math for the GPU"
+ * (the dense matrix as a safety valve for overflowing tokens). */
 int twell_spmm(const twell_shape* shape, const twell_hybrid* in, const void* w_down, void* y,
                void* stream);
 

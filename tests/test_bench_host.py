@@ -45,3 +45,18 @@ def test_conversion_bytes_counts_h_twell_and_dense_rows_once():
     assert bench.conversion_bytes(2, 512, 256, 8, 2, 1) == 2048 + 100 + 1024
     # no dense rows, fp32, T = C = 64: h 64*4, TwELL 1 tile * (64*4 + 64 + 1)
     assert bench.conversion_bytes(1, 64, 64, 64, 4, 0) == 256 + 321
+
+
+def test_cpu_baseline_reports_affinity_cores_and_blas():
+    from activation_sparse_transformer_amd.synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS["tiny_fp32"]
+    r = bench.cpu_oracle_baseline(make_inputs(cfg), cfg, target_s=0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert r["cores"] == len(os.sched_getaffinity(0))
+    assert r["blas"]["build"]  # the BLAS NumPy was built against is named
+
+
+def test_median_and_percentiles():
+    assert bench.median([3.0, 1.0, 2.0, 100.0, 4.0]) == 3.0
+    assert bench.percentile([1, 2, 3, 4, 5], 50) == 3.0

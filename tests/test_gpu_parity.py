@@ -204,6 +204,67 @@ def test_spmm_large_fallback_tiles_integer_exact():
     np.testing.assert_array_equal(as_f32(y), y_ref)
 
 
+@pytest.mark.parametrize("dtype,n,dm", [("fp32", 1200, 512), ("bf16", 1500, 136)])
+def test_spmm_wave_per_chunk_integer_exact(dtype, n, dm):
+    """Enough (row, 64-lane column chunk) pairs (more than 1024) that the
+    sparse product runs one wave per pair: float32 at any width, bf16 at a
+    d_model the XCD-sliced kernel does not take.  Every value of y checked,
+    all products and sums exact."""
+    say(f"spmm wave-per-chunk {dtype} n={n} dm={dm}")
+    rng = np.random.default_rng(n + dm + 7)
+    T, C, dff = 128, 4, 1024
+    h = rng.integers(-2, 3, size=(n, dff)).astype(np.float32)
+    h[rng.random((n, dff)) >= 0.012] = 0
+    w = rng.integers(-1, 2, size=(dff, dm)).astype(np.float32)
+    w[rng.random((dff, dm)) < 0.7] = 0
+    hy, _ = twell.twell_pack(torch.from_numpy(h).to(DT[dtype]).cuda(), T, C)
+    y = twell.twell_spmm(hy, torch.from_numpy(w).to(DT[dtype]).cuda())
+    torch.cuda.synchronize()
+    ref_h = assert_pack_matches(hy, h)
+    assert 0 < ref_h.n_dense < n
+    y_ref = oracle.spmm(ref_h, w.astype(np.float64))
+    assert np.max(np.abs(y_ref)) <= 256
+    np.testing.assert_array_equal(as_f64(y), y_ref)
+
+
+@pytest.mark.parametrize("dtype,n,dm", [("bf16", 40, 1024), ("bf16", 3000, 2048),
+                                        ("fp32", 50, 136), ("fp32", 1200, 512)])
+def test_spmm_writes_each_row_once(dtype, n, dm):
+    """twell_spmm writes every row of y once: the rows listed among the stored
+    dense rows through the fallback only, every other row through the sparse
+    kernel.  A NaN sentinel in y beforehand survives nowhere; then, with the
+    stored dense rows overwritten by other values after the pack, the dense
+    rows of y follow those values (the sparse kernel does not write them
+    after, or instead of, the fallback)."""
+    say(f"spmm each row once {dtype} n={n} dm={dm}")
+    rng = np.random.default_rng(n * 3 + dm)
+    T, C, dff = 128, 4, 512
+    h = rng.integers(-2, 3, size=(n, dff)).astype(np.float32)
+    h[rng.random((n, dff)) >= 0.02] = 0
+    w = rng.integers(-1, 2, size=(dff, dm)).astype(np.float32)
+    hy, _ = twell.twell_pack(torch.from_numpy(h).to(DT[dtype]).cuda(), T, C)
+    torch.cuda.synchronize()
+    ref_h = assert_pack_matches(hy, h)
+    assert 0 < ref_h.n_dense < n
+    wd = torch.from_numpy(w).to(DT[dtype]).cuda()
+    y = torch.full((n, dm), float("nan"), dtype=DT[dtype], device="cuda")
+    twell.twell_spmm(hy, wd, out=y)
+    torch.cuda.synchronize()
+    y_ref = oracle.spmm(ref_h, w.astype(np.float64))
+    np.testing.assert_array_equal(as_f64(y), y_ref)  # no NaN sentinel survives
+    # with the stored dense rows forged to hold other values, the dense rows
+    # of y follow them: the sparse kernel wrote nothing there after the fallback
+    nd = hy.n_dense_host()
+    hy.dense_values[:nd] = 1
+    twell.twell_spmm(hy, wd, out=y)
+    torch.cuda.synchronize()
+    forged = ref_h.values.copy(), ref_h.dense_values.copy()
+    ref_h.dense_values[:] = 1
+    y_ref2 = oracle.spmm(ref_h, w.astype(np.float64))
+    ref_h.values, ref_h.dense_values = forged
+    np.testing.assert_array_equal(as_f64(y), y_ref2)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_spmm_identity_is_unpack(dtype):
     ht, hh = sparse_h(9, 90, 256, 0.05, DT[dtype])
@@ -293,6 +354,27 @@ def test_forward_small(name, n, dm, dff):
     np.testing.assert_array_equal(u32(as_f32(out2.y)), u32(as_f32(out.y)))
     np.testing.assert_array_equal(out2.hybrid.counts.cpu().numpy(), out.hybrid.counts.cpu().numpy())
     np.testing.assert_array_equal(u32(as_f32(out2.hybrid.values)), u32(as_f32(out.hybrid.values)))
+
+
+@pytest.mark.parametrize("n,dm,dff", [(300, 256, 1024), (1500, 512, 2048), (130, 136, 576)])
+def test_forward_fp32_many_rows(n, dm, dff):
+    """float32 batches of more than 64 rows: the VALU up-projection's pack with
+    partially filled tiles (0 < count <= C and count > C both occur), the
+    generic fallback and the float32 sparse kernels; pack bit-exact against
+    the oracle's packer on the GPU's own h, h and y within 1e-4."""
+    cfg = CONFIGS["tiny_fp32"].replace(n_rows=n, d_model=dm, d_ff=dff)
+    say(f"forward fp32 n={n} dm={dm} dff={dff}")
+    t = make_inputs(cfg)
+    out = run_forward(cfg, t)
+    assert int(out.status.item()) == twell.TWELL_OK
+    h_ref, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    tol = TOL[cfg.torch_dtype]
+    assert_close_rel(as_f64(out.h_debug), h_ref, tol, "h")
+    ref = assert_pack_matches(out.hybrid, as_f32(out.h_debug))
+    cnt = ref.counts
+    assert np.any((cnt > 0) & (cnt <= cfg.capacity)) and 0 < ref.n_dense < n
+    assert_close_rel(as_f64(out.y), y_ref, tol, "y")
+    say(f"  n_dense={ref.n_dense}")
 
 
 @pytest.mark.parametrize("C", [5, 8, 16, 64, 128])
@@ -411,10 +493,9 @@ def test_forward_fp32_small_batch_matches_timed_and_standalone(n_rows, d_model, 
 
 @pytest.mark.parametrize("n_rows", [16, 48, 700, 1500, 2600])
 def test_forward_timed_variant_matches_plain_call(n_rows):
-    """The event-recording variant (every stage in order on the stream) and the
-    plain call (sparse product on the auxiliary stream concurrent with the
-    fallback; at most 64 rows, inside the fallback's split-K launch) give the
-    same y and hybrid, bit for bit."""
+    """The event-recording variant (every stage in its own launches) and the
+    plain call (at most 64 rows: the sparse product inside the fallback's
+    split-K launch) give the same y and hybrid, bit for bit."""
     cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=512, d_ff=2048)
     t = make_inputs(cfg)
     d = inputs_to_device(t)

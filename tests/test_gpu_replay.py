@@ -1,7 +1,6 @@
 """Stream ordering of ffn_sparse_forward.  Captured into a HIP graph, every
 replay equals the eager call bit for bit, with eager work and
-synchronisations between replays (the capture includes the library's fork
-onto its auxiliary stream and the join back, and, at 16 rows, the split-K
+synchronisations between replays (at 16 rows the capture holds the split-K
 path); queued back to back on shared buffers, calls do not overlap."""
 import numpy as np
 import pytest
@@ -32,7 +31,7 @@ def test_graph_replays_match_eager(name, n, dm, dff):
                                  cfg.torch_dtype, torch.device("cuda:0"))
     run = lambda: twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
                                            cfg.capacity, out=bufs)
-    run()  # eager; also creates the library's auxiliary stream before any capture
+    run()  # eager reference
     torch.cuda.synchronize()
     ref = snapshot(bufs)
     assert 0 < ref[4] < n or name == "tiny_fp32"
@@ -55,9 +54,9 @@ def test_graph_replays_match_eager(name, n, dm, dff):
 def test_back_to_back_calls_on_shared_buffers():
     """Forward calls queued back to back on one stream, alternating two inputs
     and reusing the same output and workspace buffers, with no host
-    synchronisation in between: each call's sparse product (on the auxiliary
-    stream) must finish before the next call reuses the buffers.  The final
-    outputs equal a lone call's, bit for bit."""
+    synchronisation in between: each call must finish with the buffers before
+    the next call reuses them.  The final outputs equal a lone call's, bit for
+    bit."""
     cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=600, d_model=512, d_ff=2048)
     da = inputs_to_device(make_inputs(cfg))
     db = inputs_to_device(make_inputs(cfg.replace(seed=1)))
