@@ -4,6 +4,8 @@
 #include "../../include/twell.h"
 #include "kernels.h"
 
+#include <mutex>
+
 #define TWELL_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace twell {
@@ -144,6 +146,7 @@ TWELL_EXPORT const char* twell_status_string(int status) {
     case TWELL_ERR_WORKSPACE: return "workspace too small";
     case TWELL_ERR_HIP: return "HIP launch failed";
     case TWELL_ERR_DENSE_CAPACITY: return "more dense rows than dense_capacity";
+    case TWELL_ERR_SCRATCH_LIMIT: return "shape needs more than the fixed device scratch";
     default: return "unknown status";
   }
 }
@@ -273,9 +276,11 @@ TWELL_EXPORT int ffn_sparse_forward_events(const twell_shape* shape, const void*
                       workspace_bytes, d_status, stream, stage_events);
 }
 
-TWELL_EXPORT int twell_pack(const twell_shape* shape, const void* h, const twell_hybrid* out,
-                            void* workspace, size_t workspace_bytes, int32_t* d_status,
-                            void* stream) {
+namespace twell {
+namespace {
+
+int pack_impl(const twell_shape* shape, const void* h, const twell_hybrid* out, void* workspace,
+              size_t workspace_bytes, int32_t* d_status, void* stream) {
   int rc = check_shape(shape, false);
   if (rc != TWELL_OK) return rc;
   const Geometry g = geometry(shape);
@@ -289,6 +294,60 @@ TWELL_EXPORT int twell_pack(const twell_shape* shape, const void* h, const twell
   PackOut po{out->values, out->indices, out->counts, w.route.flags, nullptr, nullptr, nullptr};
   TWELL_TRY(launch_pack_tiles(g, h, eb, po, st));
   return route_and_materialize(g, eb, w, h, out, d_status, st);
+}
+
+// ---- twell_pack_noalloc: the workspace is this fixed device array, one copy
+// per GPU.  In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies get the address that hipGetSymbolAddress
+// returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = TWELL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddr {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// The current device's copy of `scratch`, or nullptr (with *err set).
+void* scratch_address(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  ScratchAddr* a = &g_scratch[dev];
+  std::call_once(a->once, [a] {
+    a->err = hipGetSymbolAddress(&a->ptr, HIP_SYMBOL(scratch));
+    if (a->err == hipSuccess && a->ptr == nullptr) a->err = hipErrorInvalidSymbol;
+  });
+  *err = a->err;
+  return a->err == hipSuccess ? a->ptr : nullptr;
+}
+
+}  // namespace
+}  // namespace twell
+
+TWELL_EXPORT int twell_pack(const twell_shape* shape, const void* h, const twell_hybrid* out,
+                            void* workspace, size_t workspace_bytes, int32_t* d_status,
+                            void* stream) {
+  return pack_impl(shape, h, out, workspace, workspace_bytes, d_status, stream);
+}
+
+TWELL_EXPORT int twell_pack_noalloc(const twell_shape* shape, const void* h,
+                                    const twell_hybrid* out, int32_t* d_status, void* stream) {
+  const int rc = check_shape(shape, false);
+  if (rc != TWELL_OK) return rc;
+  const size_t need = pack_ws_bytes(shape);
+  if (need > kScratchBytes) return TWELL_ERR_SCRATCH_LIMIT;
+  hipError_t e = hipSuccess;
+  void* ws = scratch_address(&e);
+  if (ws == nullptr) return TWELL_ERR_HIP;
+  return pack_impl(shape, h, out, ws, kScratchBytes, d_status, stream);
 }
 
 TWELL_EXPORT int twell_unpack(const twell_shape* shape, const twell_hybrid* in, void* h,

@@ -23,13 +23,15 @@ TWELL_ERR_UNSUPPORTED = -2
 TWELL_ERR_WORKSPACE = -3
 TWELL_ERR_HIP = -4
 TWELL_ERR_DENSE_CAPACITY = -5
+TWELL_ERR_SCRATCH_LIMIT = -6
+NOALLOC_SCRATCH_BYTES = 16 << 20  # TWELL_NOALLOC_SCRATCH_BYTES
 
 _DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 
 EXPORTS = (
     "twell_version", "twell_status_string", "ffn_sparse_workspace_size", "ffn_sparse_forward",
-    "ffn_sparse_forward_events", "twell_pack_workspace_size", "twell_pack", "twell_unpack",
-    "twell_spmm",
+    "ffn_sparse_forward_events", "twell_pack_workspace_size", "twell_pack", "twell_pack_noalloc",
+    "twell_unpack", "twell_spmm",
 )
 
 
@@ -79,6 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_sparse_forward_events.argtypes = [S, P, P, P, P, P, H, P, P, sz, P, P, P]
     lib.ffn_sparse_forward_events.restype = I
     lib.twell_pack.argtypes, lib.twell_pack.restype = [S, P, H, P, sz, P, P], I
+    lib.twell_pack_noalloc.argtypes, lib.twell_pack_noalloc.restype = [S, P, H, P, P], I
     lib.twell_unpack.argtypes, lib.twell_unpack.restype = [S, H, P, P], I
     lib.twell_spmm.argtypes, lib.twell_spmm.restype = [S, H, P, P, P], I
     _lib = lib
@@ -288,6 +291,29 @@ def twell_pack(h: torch.Tensor, tile: int, capacity: int, *,
     code = load().twell_pack(ctypes.byref(shape), _ptr(h), ctypes.byref(hs), _ptr(workspace),
                              workspace.numel(), _ptr(status), _stream(dev))
     _check(code, "twell_pack")
+    return out, status
+
+
+def twell_pack_noalloc(h: torch.Tensor, tile: int, capacity: int, *,
+                       dense_capacity: Optional[int] = None, out: Optional[Hybrid] = None,
+                       status: Optional[torch.Tensor] = None):
+    """dense_to_twell of h [N, d_ff] through the entry point that takes no
+    workspace and allocates nothing (the library's fixed device scratch array
+    stands in for it); returns (hybrid, device status word).  Outputs not
+    passed in are allocated here, by PyTorch, before the call."""
+    dev = h.device
+    n, dff = h.shape
+    _need(h, "h", dev)
+    shape = make_shape(n, 8, dff, tile, capacity, h.dtype)
+    if out is None:
+        out = Hybrid.empty(n, dff, tile, capacity, h.dtype, dev, dense_capacity)
+    out.validate(dev)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=dev)
+    hs = out.struct()
+    code = load().twell_pack_noalloc(ctypes.byref(shape), _ptr(h), ctypes.byref(hs), _ptr(status),
+                                     _stream(dev))
+    _check(code, "twell_pack_noalloc")
     return out, status
 
 

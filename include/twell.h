@@ -24,7 +24,8 @@
  * Conventions shared by every entry point
  *  - All array arguments are DEVICE pointers on the current HIP device,
  *    16-byte aligned, owned by the caller.  The library never allocates or
- *    frees memory and keeps no state between calls.
+ *    frees memory and keeps no state between calls (twell_pack_noalloc's
+ *    fixed device scratch array is the one exception, by design).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work on that stream and returns; nothing is
  *    synchronised on the host.  Outputs are valid once the stream reaches the
@@ -77,7 +78,8 @@ typedef enum twell_status {
   TWELL_ERR_UNSUPPORTED = -2,    /* valid TwELL geometry the library has no kernel for */
   TWELL_ERR_WORKSPACE = -3,      /* workspace smaller than the *_workspace_size query */
   TWELL_ERR_HIP = -4,            /* a HIP launch failed */
-  TWELL_ERR_DENSE_CAPACITY = -5  /* device-side: more dense rows than dense_capacity */
+  TWELL_ERR_DENSE_CAPACITY = -5, /* device-side: more dense rows than dense_capacity */
+  TWELL_ERR_SCRATCH_LIMIT = -6   /* the shape needs more than the fixed device scratch */
 } twell_status;
 
 typedef enum twell_dtype { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype;
@@ -215,6 +217,25 @@ size_t twell_pack_workspace_size(const twell_shape* shape);
  * ffn_sparse_forward. */
 int twell_pack(const twell_shape* shape, const void* h, const twell_hybrid* out,
                void* workspace, size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/* Bytes of the fixed per-device scratch array behind twell_pack_noalloc. */
+#define TWELL_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* twell_pack without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments
+ * (minus the workspace), results and errors as twell_pack; the workspace is
+ * a fixed array of TWELL_NOALLOC_SCRATCH_BYTES in the library's device code,
+ * one per GPU, held until the process ends (its address is looked up once
+ * per device, on the first call with that device current).  A shape whose
+ * twell_pack_workspace_size exceeds TWELL_NOALLOC_SCRATCH_BYTES returns
+ * TWELL_ERR_SCRATCH_LIMIT before anything is enqueued; so does a failure to
+ * look the array up (TWELL_ERR_HIP).  Every call on one GPU shares its
+ * array: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  Nothing in the array
+ * needs to start at any value: each call writes every part it reads. */
+int twell_pack_noalloc(const twell_shape* shape, const void* h, const twell_hybrid* out,
+                       int32_t* d_status, void* stream);
 
 /* twell_to_dense: h [n_rows][d_ff] = +0.0 everywhere, then every stored slot
  * (k < counts) is written to its column and every stored dense row

@@ -130,3 +130,15 @@ def test_workspace_too_small_rejected_on_host(lib):
     # a misaligned pointer is rejected before the size check
     rc = lib.twell_pack(ctypes.byref(s), a + 2, ctypes.byref(h), a, 1 << 30, None, None)
     assert rc == twell.TWELL_ERR_INVALID_ARG
+
+
+@no_gpu_only
+def test_noalloc_pack_rejects_shapes_beyond_its_scratch(lib):
+    # 262144 rows x 64 tiles of flags alone is 16 MiB: past the fixed scratch
+    s = twell.Shape(262144, 8, 64 * 128, 128, 4, 1, 0)
+    assert lib.twell_pack_workspace_size(ctypes.byref(s)) > twell.NOALLOC_SCRATCH_BYTES
+    a = 4096
+    h = twell.HybridStruct(a, a, a, None, None, a, 0)
+    assert lib.twell_pack_noalloc(ctypes.byref(s), a, ctypes.byref(h), None, None) == \
+        twell.TWELL_ERR_SCRATCH_LIMIT
+    assert "scratch" in twell.status_string(twell.TWELL_ERR_SCRATCH_LIMIT)
