@@ -17,6 +17,8 @@
 // the 16-byte fragment reads of 16 consecutive rows hit distinct banks.
 // A B operand stored [K][N] (w_down) is transposed 8x8 in registers while
 // staging, so both operands are read from LDS the same way.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "spmm_split.h"
@@ -758,6 +760,199 @@ __global__ __launch_bounds__(CF::NT) void up_pack_bf16_fast(
                                   nt, vals, idx, cnt, flags, spill, hdebug);
 }
 
+// Epilogue for waves that own whole TwELL tiles (wave tile 64 rows x 128
+// columns, T = 64 or 128, block slots staged in LDS).  In the 32x32 MFMA
+// output layout register r of block (i, j) holds, in lanes 0-31, row
+// i*32 + (r/4)*8 + r%4 and in lanes 32-63 the row 4 below, at column
+// j*32 + lane%32; one ballot per (i, r, j) is the non-zero pattern of 32
+// columns of those two rows.  A row's tile lies in this wave's own ballots,
+// so its count, overflow and every slot position are wave-local (scalar sums
+// of ballot halves plus a lane's position among the set bits below it): no
+// counts cross waves and no barrier sits between the ballots and the stores.
+// Blocks of 32 columns without a non-zero in either row are skipped by a
+// scalar branch; inside, every lane stores, lanes without a slot to write into
+// a word of their own past the staged slots (no exec-mask branches).
+template <int L>
+__device__ __forceinline__ int set_lane(int v, int val) {
+  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(val), "i"(L));
+  return v;
+}
+
+// lane `sel` (0..63, a constant once the callers' loops are unrolled) of v = val
+__device__ __forceinline__ int set_lane_dyn(int v, int val, int sel) {
+#define TW_SET(L) if (sel == L) return set_lane<L>(v, val);
+#define TW_SET8(B) TW_SET(B) TW_SET(B + 1) TW_SET(B + 2) TW_SET(B + 3) TW_SET(B + 4) TW_SET(B + 5) TW_SET(B + 6) TW_SET(B + 7)
+  TW_SET8(0) TW_SET8(8) TW_SET8(16) TW_SET8(24) TW_SET8(32) TW_SET8(40) TW_SET8(48) TW_SET8(56)
+#undef TW_SET8
+#undef TW_SET
+  return v;
+}
+
+template <class CF, int T, bool HDEBUG>
+__device__ __forceinline__ void up_pack_epilogue_wave(
+    const fast::f32x16_t (&acc)[CF::WTM / 32][CF::WTN / 32], uint8_t* __restrict__ lds,
+    const float* __restrict__ bias, int m0, int n0, int M, int N, int C, int nt,
+    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
+  constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32, BM = CF::BM;
+  static_assert(CF::WTN == 128 && FN == 4, "a wave owns 128 columns");
+  static_assert(T == 64 || T == 128, "whole tiles per wave");
+  constexpr int TPW = 128 / T;  // tiles per wave
+  constexpr int JPT = T / 32;   // 32-column blocks per tile
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  uint16_t* sv = reinterpret_cast<uint16_t*>(lds);        // [BM][kStagedSlots] (+ 64 dummies)
+  uint8_t* si = lds + (BM * kStagedSlots + kWave) * 2;     // [BM][kStagedSlots] (+ 64 dummies)
+  uint8_t* sc = si + BM * kStagedSlots + kWave;            // [BM][4]
+  uint8_t* sf = sc + BM * 4;                               // [BM][4]
+  for (int e = threadIdx.x; e < BM * kStagedSlots / 2; e += CF::NT) {
+    reinterpret_cast<uint32_t*>(sv)[e] = 0u;
+    if (e < BM * kStagedSlots / 4) reinterpret_cast<uint32_t*>(si)[e] = 0u;
+  }
+  __syncthreads();
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  const int hh = lane >> 5, c = lane & 31;
+  const int colw = n0 + wn * 128;       // first column of the wave, tile-aligned
+  const int tbw = (wn * 128) / T;        // the wave's first tile inside the block
+  const int rw0 = wm * CF::WTM;          // the wave's first row inside the block
+  const int dummy = BM * kStagedSlots + lane;  // this lane's slot for stores that do not count
+  const int row_lim = M - (m0 + rw0);    // rows of the wave below this are inside h
+  const bool wave_cols = colw < N;       // whole tiles: all 128 columns in or out (T | d_ff)
+  float bj[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = colw + j * 32 + c;
+    bj[j] = col < N ? bias[col] : 0.f;
+  }
+  int cv[TPW];  // lane q: count of row q's tile (256 = overflow)
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) cv[tt] = 0;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    uint32_t hp[FN][8];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float z0 = acc[i][j][r] + bj[j], z1 = acc[i][j][r + 1] + bj[j];
+        const f32x2_t z = {z0 > 0.f ? z0 : 0.f, z1 > 0.f ? z1 : 0.f};
+        hp[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2_t));
+      }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qa = i * 32 + (r >> 2) * 8 + (r & 3);  // row of lanes 0-31 inside the wave
+      const int q = qa + hh * 4;                       // this lane's row inside the wave
+      const bool row_ok = q < row_lim && wave_cols;
+      uint32_t v[FN];
+      uint64_t b[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        v[j] = (r & 1) ? (hp[j][r / 2] >> 16) : (hp[j][r / 2] & 0xffffu);
+        b[j] = wave_ballot(v[j] != 0u);
+      }
+      if constexpr (HDEBUG) {
+        if (row_ok)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            hdebug[static_cast<int64_t>(m0 + rw0 + q) * N + colw + j * 32 + c] =
+                static_cast<uint16_t>(v[j]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        int la[JPT], ca = 0, cb = 0;
+#pragma unroll
+        for (int jj = 0; jj < JPT; ++jj) {
+          const uint64_t m = b[tt * JPT + jj];
+          la[jj] = __popc(static_cast<uint32_t>(m));
+          ca += la[jj];
+          cb += __popc(static_cast<uint32_t>(m >> 32));
+        }
+        const bool fa = ca <= C, fb = cb <= C;
+        cv[tt] = set_lane_dyn(cv[tt], fa ? ca : 256, qa);
+        cv[tt] = set_lane_dyn(cv[tt], fb ? cb : 256, qa + 4);
+        const bool fits = hh ? fb : fa;
+        int before_a = 0, before_b = 0;
+#pragma unroll
+        for (int jj = 0; jj < JPT; ++jj) {
+          const int j = tt * JPT + jj;
+          const uint64_t m = b[j];
+          const int lb = __popc(static_cast<uint32_t>(m >> 32));
+          if (m != 0 && (fa || fb)) {  // scalar branch: a non-zero to place
+            // mbcnt_lo adds all of the low half's bits for lanes 32-63: seed
+            // those with before_b - la, lanes 0-31 with before_a
+            const int seed = hh ? before_b - la[jj] : before_a;
+            const int pos = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                static_cast<uint32_t>(m >> 32),
+                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(seed))));
+            const bool st = v[j] != 0u && fits && row_ok;
+            const int sl = st ? (rw0 + q) * kStagedSlots + (tbw + tt) * C + pos : dummy;
+            sv[sl] = static_cast<uint16_t>(v[j]);
+            si[sl] = static_cast<uint8_t>(jj * 32 + c);
+          }
+          before_a += la[jj];
+          before_b += lb;
+        }
+        if (spill != nullptr && !(fa && fb)) {  // scalar branch: a row of the pair overflowed
+#pragma unroll
+          for (int jj = 0; jj < JPT; ++jj)
+            if (!fits && row_ok)
+              spill[static_cast<int64_t>(m0 + rw0 + q) * N + colw + (tt * JPT + jj) * 32 + c] =
+                  static_cast<uint16_t>(v[tt * JPT + jj]);
+        }
+      }
+    }
+  }
+  // counts and flags of the wave's rows: lane q holds row q's
+  if (lane < CF::WTM) {
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      sc[(rw0 + lane) * 4 + tbw + tt] = static_cast<uint8_t>(cv[tt] & 0xff);
+      sf[(rw0 + lane) * 4 + tbw + tt] = static_cast<uint8_t>(cv[tt] >> 8);
+    }
+  }
+  __syncthreads();
+  // copy the block's slots out: each row owns one contiguous run per array
+  const int tpb = CF::BN / T;
+  const int t0 = n0 / T;
+  const int tv = min(tpb, nt - t0);  // tiles of the block inside d_ff
+  const int run = tv * C;
+  for (int e = threadIdx.x; e < BM * run; e += CF::NT) {
+    const int rl = e / run, k = e - (e / run) * run;
+    const int n = m0 + rl;
+    if (n < M) {
+      const int64_t g = (static_cast<int64_t>(n) * nt + t0) * C + k;
+      vals[g] = sv[rl * kStagedSlots + k];
+      idx[g] = si[rl * kStagedSlots + k];
+    }
+  }
+  for (int e = threadIdx.x; e < BM * tv; e += CF::NT) {
+    const int rl = e / tv, k = e - (e / tv) * tv;
+    const int n = m0 + rl;
+    if (n < M) {
+      cnt[static_cast<int64_t>(n) * nt + t0 + k] = sc[rl * 4 + k];
+      flags[static_cast<int64_t>(n) * nt + t0 + k] = sf[rl * 4 + k];
+    }
+  }
+}
+
+// Fast G1 with waves of 64 x 128: each wave owns whole tiles of T = 64 or 128
+// for its rows, so the pack needs no exchange between waves.
+template <class CF, int T, bool HDEBUG>
+__global__ __launch_bounds__(CF::NT) void up_pack_bf16_wave(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_up_t,
+    const float* __restrict__ bias, int M, int N, int K, int C, int nt,
+    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+  int m0, n0;
+  fast::tile_coords<4>((M + CF::BM - 1) / CF::BM, (N + CF::BN - 1) / CF::BN, CF::BM, CF::BN, m0, n0);
+  fast::f32x16_t acc[CF::WTM / 32][CF::WTN / 32];
+  fast::mainloop32<CF>(x, K, M, m0, w_up_t, K, N, n0, K, lds, acc);
+  up_pack_epilogue_wave<CF, T, HDEBUG>(acc, reinterpret_cast<uint8_t*>(lds), bias, m0, n0, M, N, C,
+                                       nt, vals, idx, cnt, flags, spill, hdebug);
+}
+
 // ---------------------------------------------------------------- G4 kernel
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 __global__ __launch_bounds__(kThreads) void fallback_bf16_kernel(
@@ -796,30 +991,75 @@ __global__ __launch_bounds__(kThreads) void fallback_bf16_kernel(
 }
 
 // Fast G4 (K = d_ff, a multiple of 64): w_down tiles go to LDS as stored and
-// are read with the transpose load.  Tiles are numbered row-block-major over
-// the worst-case row count, so the live ones (a prefix) spread over all XCDs.
+// are read with the transpose load.  The grid is sized on the host (the live
+// row count stays on the device), so each workgroup first works out the
+// split: with L live BM x BN tiles and G workgroups, K is cut into
+// S = clamp(G / L, 1, ...) slices, workgroup b taking tile b mod L (so the
+// live tiles spread over all XCDs) and slice b / L.  With S = 1 the tile is
+// rounded and scattered into y; otherwise each slice stores its fp32 partial
+// sums part[slice][m][n] for the live rows and fallback_reduce_kernel adds
+// the slices in slice order.  S depends only on the live row count and the
+// launch, so both kernels derive the same split, and the sum order is fixed.
+constexpr int kFbMaxSlices = 32;
+
+struct FbSplit {
+  int live_tiles;
+  int slices;
+};
+
+__device__ __forceinline__ FbSplit fb_split(int M, int BM, int n_blocks, int grid, int ksteps,
+                                            int N, const float* part, int64_t part_elems) {
+  FbSplit sp;
+  sp.live_tiles = ((M + BM - 1) / BM) * n_blocks;
+  int s = sp.live_tiles > 0 ? grid / sp.live_tiles : 1;
+  s = min(s, min(ksteps, kFbMaxSlices));
+  // the partial sums [s][M][N] must fit the scratch
+  if (part == nullptr || M <= 0) s = 1;
+  else s = static_cast<int>(min(static_cast<int64_t>(s), part_elems / (static_cast<int64_t>(M) * N)));
+  sp.slices = max(s, 1);
+  return sp;
+}
+
 template <class CF>
 __global__ __launch_bounds__(CF::NT) void fallback_bf16_fast(
     const uint16_t* __restrict__ dense_values, const int32_t* __restrict__ dense_rows,
     const int32_t* __restrict__ n_dense, int64_t dense_cap, const uint16_t* __restrict__ w_down,
-    uint16_t* __restrict__ y, int64_t y_rows, int N, int K) {
+    uint16_t* __restrict__ y, int64_t y_rows, int N, int K, float* __restrict__ part,
+    int64_t part_elems) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
   const int M = static_cast<int>(min(static_cast<int64_t>(*n_dense), dense_cap));
   const int n_blocks = (N + CF::BN - 1) / CF::BN;
-  const int m0 = (blockIdx.x / n_blocks) * CF::BM;
-  const int n0 = (blockIdx.x % n_blocks) * CF::BN;
-  if (m0 >= M) return;
+  const int ksteps = K / fast::BKF;
+  const FbSplit sp = fb_split(M, CF::BM, n_blocks, static_cast<int>(gridDim.x), ksteps, N, part,
+                              part_elems);
+  const int b = blockIdx.x;
+  if (M <= 0 || b >= sp.live_tiles * sp.slices) return;  // surplus workgroups leave
+  const int tile = b % sp.live_tiles, slice = b / sp.live_tiles;
+  const int m0 = (tile / n_blocks) * CF::BM;
+  const int n0 = (tile % n_blocks) * CF::BN;
+  const int k0 = (slice * ksteps / sp.slices) * fast::BKF;
+  const int k1 = ((slice + 1) * ksteps / sp.slices) * fast::BKF;
   f32x4_t acc[CF::FM][CF::FN];
-  fast::mainloop_kn<CF>(dense_values, K, M, m0, w_down, N, N, n0, K, lds, acc);
+  fast::mainloop_kn<CF>(dense_values + k0, K, M, m0, w_down + static_cast<int64_t>(k0) * N, N, N,
+                        n0, k1 - k0, lds, acc);
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  float* dst = part + static_cast<int64_t>(slice) * M * N;
 #pragma unroll
   for (int i = 0; i < CF::FM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + wm * CF::WTM + i * 16 + (lane >> 4) * 4 + r;
       if (m >= M) continue;
+      if (sp.slices > 1) {
+#pragma unroll
+        for (int j = 0; j < CF::FN; ++j) {
+          const int col = n0 + wn * CF::WTN + j * 16 + (lane & 15);
+          if (col < N) dst[static_cast<int64_t>(m) * N + col] = acc[i][j][r];
+        }
+        continue;
+      }
       const int64_t yrow = dense_rows[m];
       if (yrow < 0 || yrow >= y_rows) continue;  // never write outside y
 #pragma unroll
@@ -828,6 +1068,44 @@ __global__ __launch_bounds__(CF::NT) void fallback_bf16_fast(
         if (col < N) y[yrow * N + col] = ElemTraits<uint16_t>::from_f32(acc[i][j][r]);
       }
     }
+}
+
+// Sum of the fallback's K slices (when fallback_bf16_fast split K): thread i
+// adds 8 consecutive outputs of one live row over the slices in slice order,
+// rounds them and stores them to y[dense_rows[m]].  Launched for the worst
+// case; with S = 1 every workgroup leaves at once.
+constexpr int kFbReduceThreads = 256;
+
+__global__ __launch_bounds__(kFbReduceThreads) void fallback_reduce_kernel(
+    const float* __restrict__ part, int64_t part_elems, const int32_t* __restrict__ n_dense,
+    int64_t dense_cap, const int32_t* __restrict__ dense_rows, uint16_t* __restrict__ y,
+    int64_t y_rows, int N, int K, int BM, int BN, int split_grid) {
+  const int M = static_cast<int>(min(static_cast<int64_t>(*n_dense), dense_cap));
+  const int n_blocks = (N + BN - 1) / BN;
+  const FbSplit sp = fb_split(M, BM, n_blocks, split_grid, K / fast::BKF, N, part, part_elems);
+  if (M <= 0 || sp.slices == 1) return;
+  const int per_row = N / 8;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kFbReduceThreads + threadIdx.x;
+  if (i >= static_cast<int64_t>(M) * per_row) return;
+  const int m = static_cast<int>(i / per_row);
+  const int c = static_cast<int>(i % per_row) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int64_t slice_stride = static_cast<int64_t>(M) * N;
+  const float* src = part + static_cast<int64_t>(m) * N + c;
+  for (int s = 0; s < sp.slices; ++s) {
+    const float4 a = *reinterpret_cast<const float4*>(src + s * slice_stride);
+    const float4 b = *reinterpret_cast<const float4*>(src + s * slice_stride + 4);
+    acc[0] += a.x, acc[1] += a.y, acc[2] += a.z, acc[3] += a.w;
+    acc[4] += b.x, acc[5] += b.y, acc[6] += b.z, acc[7] += b.w;
+  }
+  const int64_t yrow = dense_rows[m];
+  if (yrow < 0 || yrow >= y_rows) return;  // never write outside y
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * q])) |
+           (static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * q + 1])) << 16);
+  *reinterpret_cast<uint4*>(y + yrow * N + c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // ------------------------------------------------- skinny split-K (bf16, <= 64 rows)
@@ -992,7 +1270,11 @@ hipError_t skinny_fallback_spmm_bf16(const Geometry& g, const uint16_t* dense_va
 // other's LDS waits; 4 waves of 128 x 128 halve the LDS reads per MFMA but
 // measured 1.45x slower at one wave per SIMD).
 typedef fast::Cfg<256, 256, 2, 4> BigCfg;
+// G1 for T = 64 and 128: the same 256 x 256 block, waves of 64 x 128
+typedef fast::Cfg<256, 256, 4, 2> BigCfgW;
 typedef fast::Cfg<128, 128, 2, 4> MidCfg;
+// workgroups of the 128 x 128 fallback when few tiles are live: two per CU
+constexpr int kFbSplitGrid = 512;
 
 }  // namespace
 
@@ -1006,7 +1288,22 @@ hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint1
   auto* vals = static_cast<uint16_t*>(out.vals);
   auto* spill = static_cast<uint16_t*>(out.spill);
   auto* hdbg = static_cast<uint16_t*>(out.h_debug);
-  if (M >= 128 && K % 64 == 0) {
+  if (M >= 128 && K % 64 == 0 && (g.tile == 64 || g.tile == 128) && N % 128 == 0 &&
+      (BigCfgW::BN / g.tile) * g.capacity <= kStagedSlots) {
+    const int blocks =
+        ((M + BigCfgW::BM - 1) / BigCfgW::BM) * ((N + BigCfgW::BN - 1) / BigCfgW::BN);
+    auto go = [&](auto t, auto dbg) {
+      up_pack_bf16_wave<BigCfgW, decltype(t)::value, decltype(dbg)::value>
+          <<<blocks, BigCfgW::NT, 0, s>>>(x, w_up_t, b_up, M, N, K, g.capacity, g.n_tiles, vals,
+                                         out.idx, out.cnt, out.flags, spill, hdbg);
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using Y = std::true_type;
+    using No = std::false_type;
+    if (g.tile == 64) hdbg ? go(I64{}, Y{}) : go(I64{}, No{});
+    else hdbg ? go(I128{}, Y{}) : go(I128{}, No{});
+  } else if (M >= 128 && K % 64 == 0) {
     const int blocks = ((M + BigCfg::BM - 1) / BigCfg::BM) * ((N + BigCfg::BN - 1) / BigCfg::BN);
     up_pack_bf16_fast<BigCfg><<<blocks, BigCfg::NT, 0, s>>>(
         x, w_up_t, b_up, M, N, K, g.tile, g.capacity, g.n_tiles, vals, out.idx, out.cnt, out.flags,
@@ -1030,7 +1327,7 @@ hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint1
 hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
                                 const int32_t* dense_rows, const int32_t* n_dense,
                                 int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
-                                hipStream_t s, float* skinny) {
+                                hipStream_t s, float* skinny, float* part, int64_t part_elems) {
   const int64_t worst = dense_cap < g.n_rows ? dense_cap : g.n_rows;
   if (worst <= 0) return hipSuccess;
   if (skinny != nullptr && g.n_rows <= kSkinnyMaxRows && g.d_ff % 64 == 0) {
@@ -1046,12 +1343,24 @@ hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
   const int64_t big_tiles = ((worst + BigCfg::BM - 1) / BigCfg::BM) * (N / BigCfg::BN);
   if (K % 64 == 0 && N % BigCfg::BN == 0 && big_tiles >= 2048) {
     fallback_bf16_fast<BigCfg><<<static_cast<int>(big_tiles), BigCfg::NT, 0, s>>>(
-        dense_values, dense_rows, n_dense, dense_cap, w_down, y, g.n_rows, N, K);
-  } else if (worst >= 128 && K % 64 == 0 && N >= 128) {
-    const int64_t blocks =
+        dense_values, dense_rows, n_dense, dense_cap, w_down, y, g.n_rows, N, K, nullptr, 0);
+  } else if (worst >= 128 && K % 64 == 0 && N >= 128 && N % 8 == 0) {
+    // the worst case's tiles, and at least two workgroups per CU so that a
+    // few live tiles split K
+    const int64_t tiles =
         ((worst + MidCfg::BM - 1) / MidCfg::BM) * ((N + MidCfg::BN - 1) / MidCfg::BN);
-    fallback_bf16_fast<MidCfg><<<static_cast<int>(blocks), MidCfg::NT, 0, s>>>(
-        dense_values, dense_rows, n_dense, dense_cap, w_down, y, g.n_rows, N, K);
+    const int grid = static_cast<int>(tiles > kFbSplitGrid ? tiles : kFbSplitGrid);
+    if (part == nullptr) part_elems = 0;
+    fallback_bf16_fast<MidCfg><<<grid, MidCfg::NT, 0, s>>>(
+        dense_values, dense_rows, n_dense, dense_cap, w_down, y, g.n_rows, N, K, part, part_elems);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || part == nullptr) return e;
+    const int64_t outs = worst * (N / 8);
+    const unsigned rblocks =
+        static_cast<unsigned>((outs + kFbReduceThreads - 1) / kFbReduceThreads);
+    fallback_reduce_kernel<<<rblocks, kFbReduceThreads, 0, s>>>(
+        part, part_elems, n_dense, dense_cap, dense_rows, y, g.n_rows, N, K, MidCfg::BM,
+        MidCfg::BN, grid);
   } else if (worst >= 128) {
     constexpr int BM = 256, BN = 256;
     const int64_t blocks = ((worst + BM - 1) / BM) * ((N + BN - 1) / BN);

@@ -159,10 +159,13 @@ hipError_t launch_spmm_sparse(const Geometry& g, int elem_bytes, const void* val
 
 // G4: y[dense_rows[m]] = dense_values[m] w_down for m < min(*n_dense, dense_cap).
 // `skinny`: skinny_ws_bytes(g) of workspace for the split-K path, or nullptr.
+// `part`: part_elems floats of scratch in which the 128 x 128 tile kernel may
+// keep the partial sums of a K split when few rows are live, or nullptr.
 hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
                                 const int32_t* dense_rows, const int32_t* n_dense,
                                 int64_t dense_cap, const uint16_t* w_down, uint16_t* y,
-                                hipStream_t s, float* skinny = nullptr);
+                                hipStream_t s, float* skinny = nullptr, float* part = nullptr,
+                                int64_t part_elems = 0);
 
 // The few-row sparse product's launch plan for workgroups of `waves` waves,
 // each taking `parts_per_wave` of the row's waves * parts_per_wave tile

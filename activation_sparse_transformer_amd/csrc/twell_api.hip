@@ -79,6 +79,11 @@ size_t fwd_ws_bytes(const twell_shape* s) {
          align_up(skinny_ws_bytes(geometry(s)));
 }
 
+// Floats that fit in the forward's spill area [N][d_ff] of dtype.
+int64_t spill_floats(const twell_shape* s) {
+  return static_cast<int64_t>(s->n_rows) * s->d_ff * elem_bytes(s->dtype) / 4;
+}
+
 PackWorkspace carve(const twell_shape* s, void* ws, bool with_spill) {
   PackWorkspace w;
   const size_t n = static_cast<size_t>(s->n_rows);
@@ -237,10 +242,12 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
     if (merged) {
       // done above
     } else if (eb == 2)
+      // the spill area has been read by step 2: step 4 may keep partial sums there
       TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(h_out->dense_values),
                                      h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,
                                      static_cast<const uint16_t*>(w_down),
-                                     static_cast<uint16_t*>(y), st, w.skinny));
+                                     static_cast<uint16_t*>(y), st, w.skinny,
+                                     static_cast<float*>(w.spill), spill_floats(shape)));
     else
       TWELL_TRY(launch_fallback_f32(g, static_cast<const float*>(h_out->dense_values),
                                     h_out->dense_rows, h_out->n_dense, h_out->dense_capacity,

@@ -377,6 +377,28 @@ def test_forward_fp32_many_rows(n, dm, dff):
     say(f"  n_dense={ref.n_dense}")
 
 
+@pytest.mark.parametrize("n,dm,dff,C", [(300, 256, 1024, 4), (260, 128, 1280, 16), (130, 192, 768, 17),
+                                         (129, 64, 576, 4)])
+def test_forward_tile64_bf16(n, dm, dff, C):
+    """bf16 with T = 64: the up-projection's waves own whole tiles (2 per wave)
+    up to 64 staged slots per block row (C <= 16); C = 17 and a d_ff that is
+    not a multiple of 128 take the other epilogue.  Pack bit-exact, h and y
+    within tolerance."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n, d_model=dm, d_ff=dff, tile=64, capacity=C)
+    say(f"forward bf16 T=64 n={n} dm={dm} dff={dff} C={C}")
+    t = make_inputs(cfg)
+    # ~4% active at C = 4, ~15% at C >= 16: tiles both fit and overflow
+    t["b_up"] = t["b_up"] + (0.6 if C <= 4 else 1.6)
+    out = run_forward(cfg, t)
+    assert int(out.status.item()) == twell.TWELL_OK
+    h_ref, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    tol = TOL[cfg.torch_dtype]
+    assert_close_rel(as_f64(out.h_debug), h_ref, tol, "h")
+    ref = assert_pack_matches(out.hybrid, as_f32(out.h_debug))
+    assert 0 < ref.n_dense < n
+    assert_close_rel(as_f64(out.y), y_ref, tol, "y")
+
+
 @pytest.mark.parametrize("C", [5, 8, 16, 64, 128])
 def test_forward_capacities(C):
     """The 1B layer's tile width with other capacities (the capacity sweep):
@@ -439,7 +461,11 @@ def test_forward_zero_rows():
 
 
 def test_forward_matches_standalone_pack_and_spmm():
-    """The fused path equals pack(h) followed by spmm, bit for bit."""
+    """The fused path's hybrid equals pack(h) bit for bit, and its y equals
+    twell_spmm of that hybrid bit for bit on the sparse rows; on the dense
+    rows within tolerance (the forward may split the fallback's K over
+    workgroups, keeping partial sums in its workspace, where twell_spmm has
+    none), both against the oracle."""
     cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=333, d_model=256, d_ff=1024)
     t = make_inputs(cfg)
     out = run_forward(cfg, t)
@@ -453,7 +479,53 @@ def test_forward_matches_standalone_pack_and_spmm():
     assert nd == out.hybrid.n_dense_host() and nd > 0
     np.testing.assert_array_equal(u32(as_f32(out.hybrid.dense_values[:nd])),
                                   u32(as_f32(hy.dense_values[:nd])))
-    np.testing.assert_array_equal(u32(as_f32(out.y)), u32(as_f32(y2)))
+    sparse = np.ones(cfg.n_rows, dtype=bool)
+    sparse[hy.dense_rows[:nd].cpu().numpy()] = False
+    np.testing.assert_array_equal(u32(as_f32(out.y))[sparse], u32(as_f32(y2))[sparse])
+    _, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    assert_close_rel(as_f64(out.y), y_ref, TOL[cfg.torch_dtype], "forward y")
+    assert_close_rel(as_f64(y2), y_ref, TOL[cfg.torch_dtype], "twell_spmm y")
+
+
+def integer_layer(seed, n, dm, dff, b0):
+    """A layer whose every intermediate is a small integer: x, W_up, W_down in
+    {-1, 0, 1}, an integer bias.  z, h and y are then exact in bf16 storage
+    and float32 accumulation in any order (|h| < 16, |y| < 64), so the
+    forward's y must equal the oracle's bit for bit however it splits and
+    orders its sums."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-1, 2, size=(n, dm)); x[rng.random((n, dm)) < 0.7] = 0
+    wu = rng.integers(-1, 2, size=(dff, dm)); wu[rng.random((dff, dm)) < 0.7] = 0
+    wd = rng.integers(-1, 2, size=(dff, dm)); wd[rng.random((dff, dm)) < 0.8] = 0
+    b = np.full(dff, float(b0))
+    t = {"x": torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16),
+         "w_up_t": torch.from_numpy(wu.astype(np.float32)).to(torch.bfloat16),
+         "b_up": torch.from_numpy(b.astype(np.float32)),
+         "w_down": torch.from_numpy(wd.astype(np.float32)).to(torch.bfloat16)}
+    return t
+
+
+@pytest.mark.parametrize("n,b0", [(2000, -10), (2000, -11), (300, -10), (150, -11), (40, -10)])
+def test_forward_integer_valued_exact(n, b0):
+    """Every stage on integer-valued data, y bit-exact against the oracle:
+    about 20% of the rows dense at b0 = -10, about 2% at b0 = -11 (few live
+    fallback tiles, so the fallback splits K over many workgroups), 40 rows
+    on the split-K small-batch kernels."""
+    dm, dff, T, C = 512, 2048, 128, 4
+    say(f"forward integer-valued n={n} b0={b0}")
+    t = integer_layer(n + 17 * dff, n, dm, dff, b0)
+    d = inputs_to_device(t)
+    out = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], T, C,
+                                   debug_h=True)
+    torch.cuda.synchronize()
+    assert int(out.status.item()) == twell.TWELL_OK
+    h_ref, y_ref = oracle.ffn_forward(*oracle_inputs(t))
+    assert np.max(h_ref) < 16 and np.max(np.abs(y_ref)) < 64
+    np.testing.assert_array_equal(as_f64(out.h_debug), h_ref)
+    ref = assert_pack_matches(out.hybrid, as_f32(out.h_debug))
+    assert 0 < ref.n_dense < n
+    np.testing.assert_array_equal(as_f64(out.y), y_ref)
+    say(f"  n_dense={ref.n_dense}")
 
 
 @pytest.mark.parametrize("n_rows,d_model,d_ff", [(64, 128, 512), (45, 72, 320), (33, 512, 2560),
