@@ -325,6 +325,155 @@ __device__ __forceinline__ void mainloop32(const uint16_t* __restrict__ A, int64
   __syncthreads();  // operand stages are free for the epilogue
 }
 
+// ---- software-pipelined form of mainloop32 for waves of 64 x 128 (2 x 4
+// blocks of 32x32).  Each 16-wide K step is one asm block: the 8 MFMAs of the
+// fragments in hand with the 6 ds_reads of the next step's fragments between
+// them, and a wait for those reads at its end (so no read is in flight when
+// the block ends).  The MFMAs of a stage's last step run after the next
+// stage's barrier, beside the reads of its first step.  Same products in the
+// same K order as mainloop32, so the same bits.
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+
+struct Frags24 {
+  i32x4_t a[2], b[4];
+};
+
+__device__ __forceinline__ void pipe_step(f32x16_t (&c)[2][4], const Frags24& cur, Frags24& nxt,
+                                          const uint32_t (&ad)[6]) {
+  asm volatile(
+      "ds_read_b128 %[na0], %[p0]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
+      "ds_read_b128 %[na1], %[p1]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
+      "ds_read_b128 %[nb0], %[p2]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
+      "ds_read_b128 %[nb1], %[p3]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
+      "ds_read_b128 %[nb2], %[p4]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
+      "ds_read_b128 %[nb3], %[p5]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [c00] "+v"(c[0][0]), [c01] "+v"(c[0][1]), [c02] "+v"(c[0][2]), [c03] "+v"(c[0][3]),
+        [c10] "+v"(c[1][0]), [c11] "+v"(c[1][1]), [c12] "+v"(c[1][2]), [c13] "+v"(c[1][3]),
+        [na0] "=&v"(nxt.a[0]), [na1] "=&v"(nxt.a[1]), [nb0] "=&v"(nxt.b[0]),
+        [nb1] "=&v"(nxt.b[1]), [nb2] "=&v"(nxt.b[2]), [nb3] "=&v"(nxt.b[3])
+      : [a0] "v"(cur.a[0]), [a1] "v"(cur.a[1]), [b0] "v"(cur.b[0]), [b1] "v"(cur.b[1]),
+        [b2] "v"(cur.b[2]), [b3] "v"(cur.b[3]), [p0] "v"(ad[0]), [p1] "v"(ad[1]), [p2] "v"(ad[2]),
+        [p3] "v"(ad[3]), [p4] "v"(ad[4]), [p5] "v"(ad[5]));
+}
+
+__device__ __forceinline__ void pipe_last(f32x16_t (&c)[2][4], const Frags24& cur) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %[c00], %[a0], %[b0], %[c00]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c01], %[a0], %[b1], %[c01]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c02], %[a0], %[b2], %[c02]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c03], %[a0], %[b3], %[c03]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c10], %[a1], %[b0], %[c10]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c11], %[a1], %[b1], %[c11]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c12], %[a1], %[b2], %[c12]\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[c13], %[a1], %[b3], %[c13]\n\t"
+      : [c00] "+v"(c[0][0]), [c01] "+v"(c[0][1]), [c02] "+v"(c[0][2]), [c03] "+v"(c[0][3]),
+        [c10] "+v"(c[1][0]), [c11] "+v"(c[1][1]), [c12] "+v"(c[1][2]), [c13] "+v"(c[1][3])
+      : [a0] "v"(cur.a[0]), [a1] "v"(cur.a[1]), [b0] "v"(cur.b[0]), [b1] "v"(cur.b[1]),
+        [b2] "v"(cur.b[2]), [b3] "v"(cur.b[3]));
+}
+
+__device__ __forceinline__ void pipe_load(Frags24& nxt, const uint32_t (&ad)[6]) {
+  asm volatile(
+      "ds_read_b128 %[na0], %[p0]\n\t"
+      "ds_read_b128 %[na1], %[p1]\n\t"
+      "ds_read_b128 %[nb0], %[p2]\n\t"
+      "ds_read_b128 %[nb1], %[p3]\n\t"
+      "ds_read_b128 %[nb2], %[p4]\n\t"
+      "ds_read_b128 %[nb3], %[p5]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      : [na0] "=&v"(nxt.a[0]), [na1] "=&v"(nxt.a[1]), [nb0] "=&v"(nxt.b[0]),
+        [nb1] "=&v"(nxt.b[1]), [nb2] "=&v"(nxt.b[2]), [nb3] "=&v"(nxt.b[3])
+      : [p0] "v"(ad[0]), [p1] "v"(ad[1]), [p2] "v"(ad[2]), [p3] "v"(ad[3]), [p4] "v"(ad[4]),
+        [p5] "v"(ad[5]));
+}
+
+// The accumulators start at `init` (the bias of each column) instead of 0.
+template <class CF>
+__device__ __forceinline__ void mainloop32_pipe(const uint16_t* __restrict__ A, int64_t lda, int M,
+                                                int m0, const uint16_t* __restrict__ B,
+                                                int64_t ldb, int N, int n0, int K, uint16_t* lds,
+                                                const float (&init)[4], f32x16_t (&acc)[2][4]) {
+  static_assert(CF::WTM == 64 && CF::WTN == 128, "2 x 4 blocks of 32x32 per wave");
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = init[j];
+  // VALU writes of the accumulators, then MFMAs that read them (in asm)
+  asm volatile("s_nop 15\n\ts_nop 15" ::);
+  const uint16_t* asrc[CF::A_ISSUE];
+  const uint16_t* bsrc[CF::B_ISSUE];
+  dma_sources<CF::A_ISSUE, CF::NW>(A, lda, M, m0, asrc);
+  dma_sources<CF::B_ISSUE, CF::NW>(B, ldb, N, n0, bsrc);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  const uint32_t lbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_u16*)lds));
+  // LDS byte addresses of the fragments of each 16-wide K step in stage 0
+  uint32_t addr[4][6];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int kc = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      addr[ks][i] = lbase + 2u * tofs(wm * CF::WTM + i * 32 + (lane & 31), kc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      addr[ks][2 + j] = lbase + 2u * (CF::BM * BKF + tofs(wn * CF::WTN + j * 32 + (lane & 31), kc));
+  }
+  const int KT = K / BKF;
+  Frags24 f0, f1;
+  dma_issue<CF::A_ISSUE, CF::NW>(asrc, 0, lds);
+  dma_issue<CF::B_ISSUE, CF::NW>(bsrc, 0, lds + CF::BM * BKF);
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+  __syncthreads();
+  if (KT > 1) {
+    dma_issue<CF::A_ISSUE, CF::NW>(asrc, BKF, lds + CF::STAGE);
+    dma_issue<CF::B_ISSUE, CF::NW>(bsrc, BKF, lds + CF::STAGE + CF::BM * BKF);
+  }
+  pipe_load(f0, addr[0]);
+  pipe_step(acc, f0, f1, addr[1]);
+  pipe_step(acc, f1, f0, addr[2]);
+  pipe_step(acc, f0, f1, addr[3]);
+  // f1 holds the fragments of the last step of tile kt - 1
+  for (int kt = 1; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this thread's copies of tile kt landed
+    __syncthreads();  // everyone's landed, and everyone is done with tile kt-1's stage
+    if (kt + 1 < KT) {
+      uint16_t* nxt = lds + ((kt + 1) & 1) * CF::STAGE;
+      dma_issue<CF::A_ISSUE, CF::NW>(asrc, (kt + 1) * BKF, nxt);
+      dma_issue<CF::B_ISSUE, CF::NW>(bsrc, (kt + 1) * BKF, nxt + CF::BM * BKF);
+    }
+    const uint32_t so = static_cast<uint32_t>(kt & 1) * (CF::STAGE * 2);
+    uint32_t a0[6], a1[6], a2[6], a3[6];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      a0[q] = addr[0][q] + so;
+      a1[q] = addr[1][q] + so;
+      a2[q] = addr[2][q] + so;
+      a3[q] = addr[3][q] + so;
+    }
+    pipe_step(acc, f1, f0, a0);  // last step of tile kt - 1, reads of tile kt's first
+    pipe_step(acc, f0, f1, a1);
+    pipe_step(acc, f1, f0, a2);
+    pipe_step(acc, f0, f1, a3);
+  }
+  pipe_last(acc, f1);
+  // MFMA results, then VALU reads of them (outside asm)
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::);
+  __syncthreads();  // operand stages are free for the epilogue
+}
+
 // ---- [K][N] operand through LDS as stored, read with the gfx950 transpose load
 // The tile holds BKF rows (k) of BN columns (n), N-contiguous, in 32-byte
 // chunks; chunk c of row k sits at position c ^ tswz(k), so the 4 rows x 32 B
@@ -791,7 +940,7 @@ __device__ __forceinline__ int set_lane_dyn(int v, int val, int sel) {
 template <class CF, int T, bool HDEBUG>
 __device__ __forceinline__ void up_pack_epilogue_wave(
     const fast::f32x16_t (&acc)[CF::WTM / 32][CF::WTN / 32], uint8_t* __restrict__ lds,
-    const float* __restrict__ bias, int m0, int n0, int M, int N, int C, int nt,
+    int m0, int n0, int M, int N, int C, int nt,
     uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
     uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
   constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32, BM = CF::BM;
@@ -819,12 +968,6 @@ __device__ __forceinline__ void up_pack_epilogue_wave(
   const int dummy = BM * kStagedSlots + lane;  // this lane's slot for stores that do not count
   const int row_lim = M - (m0 + rw0);    // rows of the wave below this are inside h
   const bool wave_cols = colw < N;       // whole tiles: all 128 columns in or out (T | d_ff)
-  float bj[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = colw + j * 32 + c;
-    bj[j] = col < N ? bias[col] : 0.f;
-  }
   int cv[TPW];  // lane q: count of row q's tile (256 = overflow)
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) cv[tt] = 0;
@@ -835,7 +978,7 @@ __device__ __forceinline__ void up_pack_epilogue_wave(
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float z0 = acc[i][j][r] + bj[j], z1 = acc[i][j][r + 1] + bj[j];
+        const float z0 = acc[i][j][r], z1 = acc[i][j][r + 1];  // the bias is already in
         const f32x2_t z = {z0 > 0.f ? z0 : 0.f, z1 > 0.f ? z1 : 0.f};
         hp[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2_t));
       }
@@ -948,9 +1091,18 @@ __global__ __launch_bounds__(CF::NT) void up_pack_bf16_wave(
   int m0, n0;
   fast::tile_coords<4>((M + CF::BM - 1) / CF::BM, (N + CF::BN - 1) / CF::BN, CF::BM, CF::BN, m0, n0);
   fast::f32x16_t acc[CF::WTM / 32][CF::WTN / 32];
-  fast::mainloop32<CF>(x, K, M, m0, w_up_t, K, N, n0, K, lds, acc);
-  up_pack_epilogue_wave<CF, T, HDEBUG>(acc, reinterpret_cast<uint8_t*>(lds), bias, m0, n0, M, N, C,
-                                       nt, vals, idx, cnt, flags, spill, hdebug);
+  float bj[4];  // z starts at the bias of the lane's column in each 32-column block
+  {
+    const int wn = (threadIdx.x / kWave) % CF::WAVES_N;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * CF::WTN + j * 32 + (lane_id() & 31);
+      bj[j] = col < N ? bias[col] : 0.f;
+    }
+  }
+  fast::mainloop32_pipe<CF>(x, K, M, m0, w_up_t, K, N, n0, K, lds, bj, acc);
+  up_pack_epilogue_wave<CF, T, HDEBUG>(acc, reinterpret_cast<uint8_t*>(lds), m0, n0, M, N, C, nt,
+                                       vals, idx, cnt, flags, spill, hdebug);
 }
 
 // ---------------------------------------------------------------- G4 kernel
