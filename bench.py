@@ -149,12 +149,7 @@ def time_forward_warm(cfg, d, bufs, steps):
 
 def time_dense(d, steps, warmup, flush):
     """The same layer as a dense bf16 FFN through torch (hipBLASLt), cold cache."""
-    b16 = d["b_up"].to(d["x"].dtype)
-
-    def run():
-        h = torch.nn.functional.linear(d["x"], d["w_up_t"], b16)
-        torch.relu_(h)
-        return torch.matmul(h, d["w_down"])
+    run = dense_ffn(d)
 
     for i in range(warmup):
         flush_cache(flush, i)
@@ -289,6 +284,155 @@ def time_conversions(cfg, steps, warmup, flush, dev, t=None):
     return out
 
 
+# ----------------------------------------------------------------- energy
+# Energy per token of the sparse forward and of the dense torch FFN, from the
+# GPU's own power telemetry (amdsmi): each is run back to back (no cache
+# eviction between calls, so both see the same warm weights) for a few
+# seconds with a bounded queue, so the GPU never idles inside the window.  A
+# background thread samples the socket power every 10 ms and takes two
+# snapshots of the energy accumulator inside the busy window; each snapshot
+# carries its own timestamp, so the accumulator gives the exact mean power
+# between them.  J/token = mean power x loop time / tokens.  The idle power
+# before the loops is reported beside them (socket power includes it).
+ENERGY_SECONDS = 4.0
+# the decode-sized layer is measured too: there both weights stream once per call
+ENERGY_SECOND_WORKLOAD = "decode_bf16"
+
+
+class _PowerSampler:
+    def __init__(self, amdsmi, handle, t_busy0: float, t_busy1: float):
+        import threading
+        self.a, self.h = amdsmi, handle
+        self.t0, self.t1 = t_busy0, t_busy1
+        self.samples, self.snaps = [], []
+        self.stop = threading.Event()
+        self.th = threading.Thread(target=self.run, daemon=True)
+
+    def run(self):
+        snap_at = [self.t0, self.t1]
+        while not self.stop.is_set():
+            now = time.perf_counter()
+            try:
+                if self.t0 <= now <= self.t1:
+                    p = self.a.amdsmi_get_power_info(self.h).get("current_socket_power")
+                    if isinstance(p, (int, float)):
+                        self.samples.append(float(p))
+                if snap_at and now >= snap_at[0]:
+                    e = self.a.amdsmi_get_energy_count(self.h)
+                    self.snaps.append((now, e["energy_accumulator"], e["counter_resolution"],
+                                       e["timestamp"]))
+                    snap_at.pop(0)
+            except Exception:  # pragma: no cover - telemetry hiccup: keep sampling
+                pass
+            time.sleep(0.01)
+
+
+def _busy_loop(fn, seconds: float, sampler_factory):
+    """Run fn() back to back for about `seconds` with at most ~64 calls queued."""
+    fn()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(10):
+        fn()
+    torch.cuda.synchronize()
+    per_call = (time.perf_counter() - t) / 10
+    n = max(20, int(seconds / per_call))
+    start = time.perf_counter()
+    sampler = sampler_factory(start + 1.2, start + max(1.5, seconds - 0.4))
+    sampler.th.start()
+    ev = [None] * 64
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn()
+        k = i % 64
+        if ev[k] is not None:
+            ev[k].synchronize()  # keeps the queue bounded; the GPU still has 63 calls queued
+        ev[k] = torch.cuda.Event()
+        ev[k].record()
+    b.record()
+    torch.cuda.synchronize()
+    sampler.stop.set()
+    sampler.th.join()
+    return a.elapsed_time(b) * 1e-3, n, sampler
+
+
+def idle_power():
+    """Mean socket power over 1 s with the GPU idle (telemetry lags about a
+    second, so this runs before any timed work)."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        time.sleep(1.5)
+        idle = []
+        for _ in range(50):
+            p = amdsmi.amdsmi_get_power_info(h).get("current_socket_power")
+            if isinstance(p, (int, float)):
+                idle.append(float(p))
+            time.sleep(0.02)
+        amdsmi.amdsmi_shut_down()
+        return float(np.mean(idle)) if idle else None
+    except Exception:  # pragma: no cover - no telemetry on this host
+        return None
+
+
+def measure_energy(tokens_per_call: int, fns: dict, idle_w, seconds: float = ENERGY_SECONDS):
+    """J/token and mean socket power of each fn in `fns`, or the reason none
+    could be measured."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as e:  # pragma: no cover - no telemetry on this host
+        return {"error": f"amdsmi unavailable: {e!r}"}
+    try:
+        out = {"method": "socket power sampled every 10 ms and the energy accumulator read "
+                         "twice inside a back-to-back loop of about "
+                         f"{seconds:.0f} s per leg (warm cache, no eviction between calls); "
+                         "idle power measured once before any timed work",
+               "idle_socket_w": idle_w}
+        for name, fn in fns.items():
+            el, n, smp = _busy_loop(fn, seconds,
+                                    lambda t0, t1: _PowerSampler(amdsmi, h, t0, t1))
+            mean_w = float(np.mean(smp.samples)) if smp.samples else None
+            acc_w = None
+            if len(smp.snaps) == 2 and smp.snaps[1][3] > smp.snaps[0][3]:
+                (_, e0, res, ts0), (_, e1, _, ts1) = smp.snaps
+                acc_w = (e1 - e0) * res * 1e-6 / ((ts1 - ts0) * 1e-9)
+            power = acc_w if acc_w is not None else mean_w
+            tok = n * tokens_per_call
+            out[name] = {
+                "calls": n, "seconds": el, "tokens_per_s": tok / el,
+                "mean_socket_w_sampled": mean_w, "mean_socket_w_accumulator": acc_w,
+                "j_per_token": power * el / tok if power is not None else None,
+                "j_per_token_above_idle": ((power - out["idle_socket_w"]) * el / tok
+                                           if power is not None and out["idle_socket_w"] else None),
+            }
+        names = list(fns)
+        if len(names) == 2 and all(out[k]["j_per_token"] for k in names):
+            out["energy_ratio_" + names[0] + "_over_" + names[1]] = (
+                out[names[0]]["j_per_token"] / out[names[1]]["j_per_token"])
+        return out
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # pragma: no cover
+            pass
+
+
+def dense_ffn(d):
+    """The layer as a plain dense FFN through torch (hipBLASLt)."""
+    b16 = d["b_up"].to(d["x"].dtype)
+
+    def run():
+        h = torch.nn.functional.linear(d["x"], d["w_up_t"], b16)
+        torch.relu_(h)
+        return torch.matmul(h, d["w_down"])
+
+    return run
+
+
 def source_sha(stage: str) -> str:
     h = hashlib.sha256()
     for f in STAGE_SOURCES[stage]:
@@ -411,6 +555,8 @@ def main(argv=None):
                     help="slots per tile instead of the workload's own (same inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-baseline", action="store_true")
+    ap.add_argument("--no-energy", action="store_true",
+                    help="skip the energy-per-token legs (amdsmi power telemetry)")
     ap.add_argument("--no-layers", action="store_true",
                     help="skip the other workloads timed beside the headline one")
     ap.add_argument("--no-conversions", action="store_true",
@@ -432,6 +578,7 @@ def main(argv=None):
     d = {k: v.to(dev) for k, v in t.items()}
     bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
                                  cfg.torch_dtype, dev)
+    idle_w = None if args.no_energy else idle_power()
     flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
     # A plain device copy of known size (256 MiB read + 256 MiB written), run
     # once so that hardware-counter runs of this script can calibrate the
@@ -549,9 +696,27 @@ def main(argv=None):
             "mfma_frac": 4.0 * N * dm * dff / (dms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "speedup_twell_over_dense": dms / ms,
         }
+    if not args.no_energy:
+        log("[bench] energy per token: sparse forward and dense FFN")
+        fwd = lambda: twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"],
+                                               cfg.tile, cfg.capacity, out=bufs)
+        result["energy"] = {cfg.name: measure_energy(N, {"twell": fwd, "dense": dense_ffn(d)},
+                                                     idle_w)}
     if "d" in locals():
         del d, bufs
     torch.cuda.empty_cache()
+    if not args.no_energy and cfg.name != ENERGY_SECOND_WORKLOAD:
+        ec = CONFIGS[ENERGY_SECOND_WORKLOAD]
+        ed = {k: v.to(dev) for k, v in make_inputs(ec).items()}
+        eb = twell.forward_buffers(ec.n_rows, ec.d_model, ec.d_ff, ec.tile, ec.capacity,
+                                   ec.torch_dtype, dev)
+        efwd = lambda: twell.ffn_sparse_forward(ed["x"], ed["w_up_t"], ed["b_up"], ed["w_down"],
+                                                ec.tile, ec.capacity, out=eb)
+        log(f"[bench] energy per token: {ec.name}")
+        result["energy"][ec.name] = measure_energy(ec.n_rows, {"twell": efwd,
+                                                               "dense": dense_ffn(ed)}, idle_w)
+        del ed, eb
+        torch.cuda.empty_cache()
     large_inputs = None
     if not args.no_layers:
         result["layers"] = {}
