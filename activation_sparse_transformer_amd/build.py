@@ -21,7 +21,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtwell.so")
 ARCH = "gfx950"
 
-SOURCES = ["twell_api.hip", "gemm_bf16.hip", "gemm_f32.hip", "route.hip", "spmm.hip", "skinny.hip"]
+SOURCES = ["twell_api.hip", "gemm_bf16.hip", "gemm_f32.hip", "route.hip", "spmm.hip", "skinny.hip",
+           "ell.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

@@ -202,4 +202,21 @@ hipError_t launch_fallback_f32(const Geometry& g, const float* dense_values,
                                int64_t dense_cap, const float* w_down, float* y, hipStream_t s,
                                float* skinny = nullptr);
 
+// ELL rows (one tile spanning the row, 16-bit columns; g.capacity = width W).
+// Pack: counts, routing (rb.flags holds one flag per row), slots / dense rows.
+hipError_t launch_ell_pack(const Geometry& g, int elem_bytes, const void* h, const RouteBufs& rb,
+                           void* vals, uint16_t* cols, uint16_t* cnt, int32_t* dense_rows,
+                           void* dense_values, int64_t dense_cap, int32_t* n_dense,
+                           int32_t* status, hipStream_t s);
+// LDS bytes the unpack kernel needs (one row of h).
+size_t ell_unpack_lds_bytes(const Geometry& g, int elem_bytes);
+hipError_t launch_ell_unpack(const Geometry& g, int elem_bytes, const void* vals,
+                             const uint16_t* cols, const uint16_t* cnt, const int32_t* dense_rows,
+                             const void* dense_values, const int32_t* n_dense, int64_t dense_cap,
+                             void* h, hipStream_t s);
+// y of every row that `skip` does not list, from its slots.
+hipError_t launch_ell_spmm_sparse(const Geometry& g, int elem_bytes, const void* vals,
+                                  const uint16_t* cols, const uint16_t* cnt, const DenseSkip& skip,
+                                  const void* w_down, void* y, hipStream_t s);
+
 }  // namespace twell

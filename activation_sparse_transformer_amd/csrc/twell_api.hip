@@ -34,6 +34,31 @@ int check_shape(const twell_shape* s, bool need_model) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ELL rows: one tile spanning the row (tile == d_ff), capacity = width.
+int check_ell_shape(const twell_shape* s, bool need_model) {
+  if (s == nullptr) return TWELL_ERR_INVALID_ARG;
+  if (s->n_rows < 0 || s->n_rows > INT32_MAX) return TWELL_ERR_INVALID_ARG;
+  if (s->dtype != TWELL_F32 && s->dtype != TWELL_BF16) return TWELL_ERR_INVALID_ARG;
+  if (s->reserved != 0) return TWELL_ERR_INVALID_ARG;
+  if (s->d_ff <= 0 || s->d_ff > 65536 || s->d_ff % 8 != 0 || s->tile != s->d_ff)
+    return TWELL_ERR_INVALID_ARG;
+  if (s->capacity < 1 || s->capacity > s->d_ff || s->capacity > 65535) return TWELL_ERR_INVALID_ARG;
+  if (need_model && (s->d_model <= 0 || s->d_model % 8 != 0)) return TWELL_ERR_INVALID_ARG;
+  return TWELL_OK;
+}
+
+int check_ell(const twell_ell* e, int64_t n_rows) {
+  if (e == nullptr || e->n_dense == nullptr || e->dense_capacity < 0) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(e->values) || !aligned16(e->columns) || !aligned16(e->counts) ||
+      !aligned16(e->dense_rows) || !aligned16(e->dense_values))
+    return TWELL_ERR_INVALID_ARG;
+  if (n_rows > 0 && (e->values == nullptr || e->columns == nullptr || e->counts == nullptr))
+    return TWELL_ERR_INVALID_ARG;
+  if (e->dense_capacity > 0 && (e->dense_rows == nullptr || e->dense_values == nullptr))
+    return TWELL_ERR_INVALID_ARG;
+  return TWELL_OK;
+}
+
 int check_hybrid(const twell_hybrid* h, int64_t n_rows) {
   if (h == nullptr || h->n_dense == nullptr || h->dense_capacity < 0) return TWELL_ERR_INVALID_ARG;
   if (!aligned16(h->values) || !aligned16(h->indices) || !aligned16(h->counts) ||
@@ -181,8 +206,9 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
   const Geometry g = geometry(shape);
   if ((rc = check_hybrid(h_out, g.n_rows)) != TWELL_OK) return rc;
   if (g.n_rows > 0 && (x == nullptr || w_up_t == nullptr || b_up == nullptr || w_down == nullptr ||
-                       y == nullptr || workspace == nullptr))
+                       y == nullptr))
     return TWELL_ERR_INVALID_ARG;
+  if (workspace == nullptr) return TWELL_ERR_INVALID_ARG;  // the routing writes it even for 0 rows
   if (!aligned16(x) || !aligned16(w_up_t) || !aligned16(w_down) || !aligned16(y) ||
       !aligned16(h_dense_debug) || !aligned16(workspace))
     return TWELL_ERR_INVALID_ARG;
@@ -292,7 +318,7 @@ int pack_impl(const twell_shape* shape, const void* h, const twell_hybrid* out, 
   if (rc != TWELL_OK) return rc;
   const Geometry g = geometry(shape);
   if ((rc = check_hybrid(out, g.n_rows)) != TWELL_OK) return rc;
-  if (g.n_rows > 0 && (h == nullptr || workspace == nullptr)) return TWELL_ERR_INVALID_ARG;
+  if ((g.n_rows > 0 && h == nullptr) || workspace == nullptr) return TWELL_ERR_INVALID_ARG;
   if (!aligned16(h) || !aligned16(workspace)) return TWELL_ERR_INVALID_ARG;
   if (workspace_bytes < pack_ws_bytes(shape)) return TWELL_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -385,6 +411,70 @@ TWELL_EXPORT int twell_spmm(const twell_shape* shape, const twell_hybrid* in, co
   const DenseSkip skip{in->dense_rows, in->n_dense, in->dense_capacity};
   TWELL_TRY(launch_spmm_sparse(g, eb, in->values, in->indices, in->counts, nullptr, nullptr,
                                in->dense_capacity > 0 ? &skip : nullptr, w_down, y, st));
+  // ... and the stored dense rows by the dense fallback GEMM
+  if (eb == 2)
+    TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(in->dense_values),
+                                   in->dense_rows, in->n_dense, in->dense_capacity,
+                                   static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y),
+                                   st));
+  else
+    TWELL_TRY(launch_fallback_f32(g, static_cast<const float*>(in->dense_values), in->dense_rows,
+                                  in->n_dense, in->dense_capacity,
+                                  static_cast<const float*>(w_down), static_cast<float*>(y), st));
+  return TWELL_OK;
+}
+
+// ------------------------------------------------------------------ ELL rows
+TWELL_EXPORT size_t ell_pack_workspace_size(const twell_shape* shape) {
+  if (check_ell_shape(shape, false) != TWELL_OK) return 0;
+  return pack_ws_bytes(shape);  // one "tile" per row: one flag per row
+}
+
+TWELL_EXPORT int ell_pack(const twell_shape* shape, const void* h, const twell_ell* out,
+                          void* workspace, size_t workspace_bytes, int32_t* d_status,
+                          void* stream) {
+  int rc = check_ell_shape(shape, false);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_ell(out, g.n_rows)) != TWELL_OK) return rc;
+  if ((g.n_rows > 0 && h == nullptr) || workspace == nullptr) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(workspace)) return TWELL_ERR_INVALID_ARG;
+  if (workspace_bytes < pack_ws_bytes(shape)) return TWELL_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const PackWorkspace w = carve(shape, workspace, false);
+  return hip_status(launch_ell_pack(g, elem_bytes(shape->dtype), h, w.route, out->values,
+                                    out->columns, out->counts, out->dense_rows, out->dense_values,
+                                    out->dense_capacity, out->n_dense, d_status, st));
+}
+
+TWELL_EXPORT int ell_unpack(const twell_shape* shape, const twell_ell* in, void* h, void* stream) {
+  int rc = check_ell_shape(shape, false);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_ell(in, g.n_rows)) != TWELL_OK) return rc;
+  if (g.n_rows > 0 && h == nullptr) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(h)) return TWELL_ERR_INVALID_ARG;
+  if (ell_unpack_lds_bytes(g, elem_bytes(shape->dtype)) > 64 * 1024) return TWELL_ERR_UNSUPPORTED;
+  return hip_status(launch_ell_unpack(g, elem_bytes(shape->dtype), in->values, in->columns,
+                                      in->counts, in->dense_rows, in->dense_values, in->n_dense,
+                                      in->dense_capacity, h, static_cast<hipStream_t>(stream)));
+}
+
+TWELL_EXPORT int ell_spmm(const twell_shape* shape, const twell_ell* in, const void* w_down,
+                          void* y, void* stream) {
+  int rc = check_ell_shape(shape, true);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_ell(in, g.n_rows)) != TWELL_OK) return rc;
+  if (g.n_rows > 0 && (w_down == nullptr || y == nullptr)) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(w_down) || !aligned16(y)) return TWELL_ERR_INVALID_ARG;
+  if (g.n_rows == 0) return TWELL_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int eb = elem_bytes(shape->dtype);
+  // the ELL rows (a row listed among the stored dense rows is skipped) ...
+  const DenseSkip skip{in->dense_rows, in->n_dense, in->dense_capacity};
+  TWELL_TRY(launch_ell_spmm_sparse(g, eb, in->values, in->columns, in->counts, skip, w_down, y,
+                                   st));
   // ... and the stored dense rows by the dense fallback GEMM
   if (eb == 2)
     TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(in->dense_values),

@@ -31,7 +31,7 @@ _DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTS = (
     "twell_version", "twell_status_string", "ffn_sparse_workspace_size", "ffn_sparse_forward",
     "ffn_sparse_forward_events", "twell_pack_workspace_size", "twell_pack", "twell_pack_noalloc",
-    "twell_unpack", "twell_spmm",
+    "twell_unpack", "twell_spmm", "ell_pack_workspace_size", "ell_pack", "ell_unpack", "ell_spmm",
 )
 
 
@@ -52,6 +52,14 @@ class Shape(ctypes.Structure):
 class HybridStruct(ctypes.Structure):
     _fields_ = [
         ("values", ctypes.c_void_p), ("indices", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+        ("dense_rows", ctypes.c_void_p), ("dense_values", ctypes.c_void_p),
+        ("n_dense", ctypes.c_void_p), ("dense_capacity", ctypes.c_int64),
+    ]
+
+
+class EllStruct(ctypes.Structure):
+    _fields_ = [
+        ("values", ctypes.c_void_p), ("columns", ctypes.c_void_p), ("counts", ctypes.c_void_p),
         ("dense_rows", ctypes.c_void_p), ("dense_values", ctypes.c_void_p),
         ("n_dense", ctypes.c_void_p), ("dense_capacity", ctypes.c_int64),
     ]
@@ -84,6 +92,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.twell_pack_noalloc.argtypes, lib.twell_pack_noalloc.restype = [S, P, H, P, P], I
     lib.twell_unpack.argtypes, lib.twell_unpack.restype = [S, H, P, P], I
     lib.twell_spmm.argtypes, lib.twell_spmm.restype = [S, H, P, P, P], I
+    E = ctypes.POINTER(EllStruct)
+    lib.ell_pack_workspace_size.argtypes, lib.ell_pack_workspace_size.restype = [S], sz
+    lib.ell_pack.argtypes, lib.ell_pack.restype = [S, P, E, P, sz, P, P], I
+    lib.ell_unpack.argtypes, lib.ell_unpack.restype = [S, E, P, P], I
+    lib.ell_spmm.argtypes, lib.ell_spmm.restype = [S, E, P, P, P], I
     _lib = lib
     return lib
 
@@ -344,4 +357,122 @@ def twell_spmm(hy: Hybrid, w_down: torch.Tensor, out: Optional[torch.Tensor] = N
     hs = hy.struct()
     _check(load().twell_spmm(ctypes.byref(shape), ctypes.byref(hs), _ptr(w_down), _ptr(out),
                              _stream(dev)), "twell_spmm")
+    return out
+
+
+# ------------------------------------------------------------------ ELL rows
+@dataclasses.dataclass
+class Ell:
+    """Device tensors of ELL rows (see twell_ell in twell.h): the non-zeros of
+    each row in column order in the first counts[n] of `width` slots."""
+
+    width: int
+    d_ff: int
+    values: torch.Tensor        # [N, width] dtype
+    columns: torch.Tensor       # [N, width] uint16 bits (torch.int16)
+    counts: torch.Tensor        # [N] uint16 bits (torch.int16)
+    dense_rows: torch.Tensor    # [dense_capacity] int32
+    dense_values: torch.Tensor  # [dense_capacity, d_ff] dtype
+    n_dense: torch.Tensor       # [1] int32
+
+    @property
+    def n_rows(self) -> int:
+        return self.counts.shape[0]
+
+    @property
+    def dense_capacity(self) -> int:
+        return self.dense_rows.shape[0]
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return self.values.dtype
+
+    @classmethod
+    def empty(cls, n_rows: int, d_ff: int, width: int, dtype: torch.dtype, device,
+              dense_capacity: Optional[int] = None) -> "Ell":
+        cap = n_rows if dense_capacity is None else dense_capacity
+        return cls(width, d_ff,
+                   torch.empty((n_rows, width), dtype=dtype, device=device),
+                   torch.empty((n_rows, width), dtype=torch.int16, device=device),
+                   torch.empty((n_rows,), dtype=torch.int16, device=device),
+                   torch.empty((cap,), dtype=torch.int32, device=device),
+                   torch.empty((cap, d_ff), dtype=dtype, device=device),
+                   torch.empty((1,), dtype=torch.int32, device=device))
+
+    def struct(self) -> EllStruct:
+        return EllStruct(_ptr(self.values), _ptr(self.columns), _ptr(self.counts),
+                         _ptr(self.dense_rows), _ptr(self.dense_values), _ptr(self.n_dense),
+                         self.dense_capacity)
+
+    def validate(self, device) -> None:
+        n, w = self.n_rows, self.width
+        _need(self.values, "values", device, shape=(n, w))
+        _need(self.columns, "columns", device, torch.int16, (n, w))
+        _need(self.counts, "counts", device, torch.int16, (n,))
+        _need(self.dense_rows, "dense_rows", device, torch.int32)
+        _need(self.dense_values, "dense_values", device, self.values.dtype,
+              (self.dense_capacity, self.d_ff))
+        _need(self.n_dense, "n_dense", device, torch.int32, (1,))
+
+    def n_dense_host(self) -> int:
+        return int(self.n_dense.item())
+
+
+def ell_shape(n_rows: int, d_model: int, d_ff: int, width: int, dtype: torch.dtype) -> Shape:
+    """ELL rows are TwELL with one tile spanning the row: tile = d_ff, capacity = width."""
+    return make_shape(n_rows, d_model, d_ff, d_ff, width, dtype)
+
+
+def ell_pack(h: torch.Tensor, width: int, *, dense_capacity: Optional[int] = None,
+             out: Optional[Ell] = None, workspace: Optional[torch.Tensor] = None,
+             status: Optional[torch.Tensor] = None):
+    """dense_to_ell of h [N, d_ff]; returns (ell, device status word)."""
+    dev = h.device
+    n, dff = h.shape
+    _need(h, "h", dev)
+    shape = ell_shape(n, 8, dff, width, h.dtype)
+    if out is None:
+        out = Ell.empty(n, dff, width, h.dtype, dev, dense_capacity)
+    out.validate(dev)
+    if workspace is None:
+        ws = int(load().ell_pack_workspace_size(ctypes.byref(shape)))
+        if ws == 0:
+            raise TwellError(TWELL_ERR_INVALID_ARG, "ell_pack_workspace_size")
+        workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=dev)
+    es = out.struct()
+    code = load().ell_pack(ctypes.byref(shape), _ptr(h), ctypes.byref(es), _ptr(workspace),
+                           workspace.numel(), _ptr(status), _stream(dev))
+    _check(code, "ell_pack")
+    return out, status
+
+
+def ell_unpack(e: Ell, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """ell_to_dense: the dense h [N, d_ff] of ELL rows."""
+    dev = e.values.device
+    e.validate(dev)
+    if out is None:
+        out = torch.empty((e.n_rows, e.d_ff), dtype=e.dtype, device=dev)
+    _need(out, "h", dev, e.dtype, (e.n_rows, e.d_ff))
+    shape = ell_shape(e.n_rows, 8, e.d_ff, e.width, e.dtype)
+    es = e.struct()
+    _check(load().ell_unpack(ctypes.byref(shape), ctypes.byref(es), _ptr(out), _stream(dev)),
+           "ell_unpack")
+    return out
+
+
+def ell_spmm(e: Ell, w_down: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The ELL down-projection y [N, d_model] = ell_to_dense(e) @ w_down."""
+    dev = e.values.device
+    e.validate(dev)
+    dff, dm = w_down.shape
+    _need(w_down, "w_down", dev, e.dtype, (e.d_ff, dm))
+    if out is None:
+        out = torch.empty((e.n_rows, dm), dtype=e.dtype, device=dev)
+    _need(out, "y", dev, e.dtype, (e.n_rows, dm))
+    shape = ell_shape(e.n_rows, dm, e.d_ff, e.width, e.dtype)
+    es = e.struct()
+    _check(load().ell_spmm(ctypes.byref(shape), ctypes.byref(es), _ptr(w_down), _ptr(out),
+                           _stream(dev)), "ell_spmm")
     return out

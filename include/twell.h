@@ -173,7 +173,8 @@ size_t ffn_sparse_workspace_size(const twell_shape* shape);
  * TwELL form; h_dense_debug, if non-NULL, receives h [n_rows][d_ff] exactly
  * as packed (for bit-exact checks; costs one extra write of h); workspace /
  * workspace_bytes: scratch of at least ffn_sparse_workspace_size(shape)
- * bytes, contents undefined on entry and exit; d_status, if non-NULL, is set
+ * bytes, never NULL (the routing writes it even for 0 rows), contents
+ * undefined on entry and exit; d_status, if non-NULL, is set
  * on the device to TWELL_OK or TWELL_ERR_DENSE_CAPACITY.  On
  * TWELL_ERR_DENSE_CAPACITY the rows past dense_capacity are neither stored
  * nor computed, so y is undefined for them; *n_dense holds the true count so
@@ -262,6 +263,56 @@ int twell_unpack(const twell_shape* shape, const twell_hybrid* in, void* h, void
  * (the dense matrix as a safety valve for overflowing tokens). */
 int twell_spmm(const twell_shape* shape, const twell_hybrid* in, const void* w_down, void* y,
                void* stream);
+
+/* ---- ELL rows: Figure 1(a) beside TwELL (Figure 1(b)) and the hybrid
+ * (Figure 1(c)) of "Sparser, Faster, Lighter Transformer Language Models
+ * (Sakana AI + NVIDIA)", Figure 1 description.  Each token row keeps its
+ * non-zeros in ascending column order in the first `counts` of `width`
+ * slots, with their 16-bit column numbers; padding slots hold +0.0 and
+ * column 0.  It is TwELL with one tile spanning the whole row, so a twell_shape
+ * describes it with tile == d_ff and capacity == width (1 <= width <=
+ * min(d_ff, 65535)); d_ff must be a multiple of 8 and at most 65536.  A row
+ * with more than `width` non-zeros goes to the dense matrix exactly as a row
+ * with an overflowing tile does in the hybrid TwELL ("Nvidia and Sakana make
+ * LLMs 30% faster by doing less math", section "Reshaping math for the GPU").
+ * Slot positions depend on the whole row, so ELL is packed from a
+ * materialised h, not from the tiled up-projection's epilogue. */
+typedef struct twell_ell {
+  void* values;          /* [n_rows][width] dtype */
+  uint16_t* columns;     /* [n_rows][width] uint16 column in [0, d_ff) */
+  uint16_t* counts;      /* [n_rows] uint16 non-zeros stored (0 for dense rows) */
+  int32_t* dense_rows;   /* [dense_capacity] int32, ascending token rows */
+  void* dense_values;    /* [dense_capacity][d_ff] dtype, the dense rows bit for bit */
+  int32_t* n_dense;      /* device int32: number of dense rows (as in twell_hybrid) */
+  int64_t dense_capacity;
+} twell_ell;
+
+/* Bytes of device workspace ell_pack needs (0 for an invalid shape): one
+ * overflow flag per row and the row routing lists. */
+size_t ell_pack_workspace_size(const twell_shape* shape);
+
+/* dense_to_ell: pack h [n_rows][d_ff] into `out` (shape: tile == d_ff,
+ * capacity == width).  Same routing, dense-row copy, status word and
+ * capacity behaviour as twell_pack; -0.0 is dropped like +0.0 in sparse
+ * rows.  Defined by the Figure 1 description (panel a) cited above. */
+int ell_pack(const twell_shape* shape, const void* h, const twell_ell* out, void* workspace,
+             size_t workspace_bytes, int32_t* d_status, void* stream);
+
+/* ell_to_dense: h [n_rows][d_ff] = +0.0 everywhere, then the first counts[n]
+ * slots of each row at their columns, and each stored dense row copied
+ * (dense_rows strictly ascending).  Rows of more than 64 KB are
+ * TWELL_ERR_UNSUPPORTED.  Defined by the Figure 1 description (panel a). */
+int ell_unpack(const twell_shape* shape, const twell_ell* in, void* h, void* stream);
+
+/* The ELL down-projection y [n_rows][d_model] = ell_to_dense(in) W_down, every
+ * row written once: rows listed among the stored dense rows by the dense
+ * fallback GEMM, the others from their slots (float32 accumulation, one
+ * rounding).  Defined by the Figure 1 description (panel a) and "The
+ * Relentless Search for Efficiency in Large-Scale Language Models", section
+ * "Mechanism of Action: Kernel-Level Optimization" (only the weight rows of
+ * non-zero activations are read). */
+int ell_spmm(const twell_shape* shape, const twell_ell* in, const void* w_down, void* y,
+             void* stream);
 
 #ifdef __cplusplus
 }

@@ -4,9 +4,12 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package; the product path never does.
 """
 from .twell_oracle import (  # noqa: F401
+    Ell,
     Hybrid,
     bf16_bits_to_f32,
+    ell_pack,
     ell_pack_textbook,
+    ell_unpack,
     ffn_forward,
     ffn_forward_rows,
     ffn_hidden,

@@ -270,3 +270,74 @@ def ell_pack_textbook(h: np.ndarray, width: int):
             vals[r, k] = h[r, c]
             cols[r, k] = c
     return vals, cols, nnz
+
+
+# --------------------------------------------------------------------------
+# ELL rows with the hybrid split: Figure 1(a) beside TwELL [wiki Figure 1]
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class Ell:
+    """A token-row matrix h [N, d_ff] as ELL rows plus dense rows.
+
+    values  [N, width]  the row's non-zeros in ascending column order, then +0
+    columns [N, width]  int64 column of each slot (0 in padding)
+    counts  [N]         int64 non-zeros stored (0 for a dense row)
+    dense_rows   [n_dense]        int32 rows with more than `width` non-zeros
+    dense_values [n_dense, d_ff]  those rows, copied bit for bit
+    """
+
+    width: int
+    d_ff: int
+    values: np.ndarray
+    columns: np.ndarray
+    counts: np.ndarray
+    dense_rows: np.ndarray
+    dense_values: np.ndarray
+
+    @property
+    def n_dense(self) -> int:
+        return int(self.dense_rows.shape[0])
+
+
+def ell_pack(h: np.ndarray, width: int) -> Ell:
+    """dense_to_ell by its definition, one row and column at a time.
+
+    A row keeps its non-zeros (tested by value, so -0.0 is zero and NaN is
+    not) in ascending column order in its first slots, padding after them;
+    a row with more than ``width`` non-zeros goes to the dense matrix whole,
+    the hybrid rule with one tile spanning the row.  Pure-Python loops: for
+    small inputs.
+    """
+    h = np.asarray(h)
+    n, d_ff = h.shape
+    if width < 1 or width > d_ff:
+        raise ValueError(f"width {width} must be in [1, d_ff]")
+    values = np.zeros((n, width), dtype=h.dtype)
+    columns = np.zeros((n, width), dtype=np.int64)
+    counts = np.zeros(n, dtype=np.int64)
+    dense_rows = []
+    for r in range(n):
+        nz = [c for c in range(d_ff) if h[r, c] != 0]
+        if len(nz) > width:
+            dense_rows.append(r)
+            continue
+        counts[r] = len(nz)
+        for k, c in enumerate(nz):
+            values[r, k] = h[r, c]
+            columns[r, k] = c
+    dense_rows = np.array(dense_rows, dtype=np.int32)
+    dense_values = h[dense_rows].copy() if len(dense_rows) else np.zeros((0, d_ff), h.dtype)
+    return Ell(width, d_ff, values, columns, counts, dense_rows, dense_values)
+
+
+def ell_unpack(e: Ell) -> np.ndarray:
+    """ell_to_dense: +0 everywhere, the first counts[n] slots of each row at their
+    columns, then the dense rows copied."""
+    n = e.counts.shape[0]
+    h = np.zeros((n, e.d_ff), dtype=e.values.dtype)
+    for r in range(n):
+        for k in range(int(e.counts[r])):
+            h[r, int(e.columns[r, k])] = e.values[r, k]
+    if e.n_dense:
+        h[e.dense_rows] = e.dense_values
+    return h

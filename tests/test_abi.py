@@ -47,7 +47,7 @@ def test_every_declared_symbol_is_exported(lib):
         assert name in exported, name
         assert hasattr(lib, name)
     # nothing else of the library's own leaks out of the ABI
-    ours = {n for n in exported if n.startswith(("twell", "ffn_"))}
+    ours = {n for n in exported if n.startswith(("twell", "ffn_", "ell_"))}
     assert ours == set(twell.EXPORTS)
 
 
