@@ -284,6 +284,84 @@ def time_conversions(cfg, steps, warmup, flush, dev, t=None):
     return out
 
 
+# ----------------------------------------------------------------- formats
+# The three panels of the Figure 1 description on the same inputs: hybrid
+# TwELL (panel c) at capacities C = 4..8, ELL rows (panel a) with the same
+# slot budget per row (width = d_ff / T * C, the hybrid split for rows over
+# it) and pure TwELL (panel b, C = T: no row ever overflows).  For each: the
+# rows sent to the dense matrix, the sparse down-projection of the packed h
+# (twell_spmm / ell_spmm, dense rows included: these standalone calls take no
+# workspace, so their dense fallback cannot split K), the pack from a
+# materialised h, and for TwELL the whole fused forward and its own
+# down-projection (steps 3 + 4, whose fallback may split K in the forward's
+# workspace).  Cold cache, median of `steps`.
+FORMAT_WORKLOADS = ("ffn_1b_bf16", "decode_bf16")
+FORMAT_CAPACITIES = (4, 5, 6, 7, 8)
+
+
+def time_formats(cfg, steps, flush, dev, caps=FORMAT_CAPACITIES):
+    t = make_inputs(cfg)
+    d = {k: v.to(dev) for k, v in t.items()}
+    del t
+    warm = 2
+    out = {"workload": cfg.name, "n_rows": cfg.n_rows, "d_ff": cfg.d_ff, "tile": cfg.tile,
+           "steps": steps, "capacities": {}}
+    h = None
+    for C in list(caps) + [cfg.tile]:
+        bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, C,
+                                     cfg.torch_dtype, dev, debug_h=h is None)
+        fwd = lambda: twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"],
+                                               cfg.tile, C, out=bufs)
+        fwd()
+        torch.cuda.synchronize()
+        if h is None:
+            h = bufs.h_debug
+            bufs.h_debug = None
+        row = {"twell_forward_ms": median(_timed_calls(fwd, steps, warm, flush)),
+               "twell_n_dense": bufs.hybrid.n_dense_host()}
+        # the forward's own down-projection: steps 3 + 4 timed with stage events
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for i in range(steps):
+            flush_cache(flush, i)
+            twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile, C,
+                                     out=bufs, stage_events=ev[i])
+        torch.cuda.synchronize()
+        row["twell_forward_downproj_ms"] = median([ev[i][2].elapsed_time(ev[i][4])
+                                                   for i in range(steps)])
+        hy = bufs.hybrid
+        ws = torch.empty((max(twell.pack_workspace_bytes(
+            twell.make_shape(cfg.n_rows, 8, cfg.d_ff, cfg.tile, C, cfg.torch_dtype)), 1),),
+            dtype=torch.uint8, device=dev)
+        st = torch.empty((1,), dtype=torch.int32, device=dev)
+        row["twell_pack_ms"] = median(_timed_calls(
+            lambda: twell.twell_pack(h, cfg.tile, C, out=hy, workspace=ws, status=st),
+            steps, warm, flush))
+        y = torch.empty((cfg.n_rows, cfg.d_model), dtype=cfg.torch_dtype, device=dev)
+        row["twell_spmm_ms"] = median(_timed_calls(lambda: twell.twell_spmm(hy, d["w_down"], out=y),
+                                                   steps, warm, flush))
+        del bufs, hy, ws
+        if C == cfg.tile:
+            out["pure_twell"] = row
+            continue
+        width = cfg.n_tiles * C
+        e = twell.Ell.empty(cfg.n_rows, cfg.d_ff, width, cfg.torch_dtype, dev)
+        ews = torch.empty((max(twell.load().ell_pack_workspace_size(
+            twell.ell_shape(cfg.n_rows, 8, cfg.d_ff, width, cfg.torch_dtype)), 1),),
+            dtype=torch.uint8, device=dev)
+        row["ell_width"] = width
+        row["ell_pack_ms"] = median(_timed_calls(
+            lambda: twell.ell_pack(h, width, out=e, workspace=ews, status=st), steps, warm, flush))
+        row["ell_n_dense"] = e.n_dense_host()
+        row["ell_spmm_ms"] = median(_timed_calls(lambda: twell.ell_spmm(e, d["w_down"], out=y),
+                                                 steps, warm, flush))
+        out["capacities"][str(C)] = row
+        del e, ews
+        torch.cuda.empty_cache()
+    del d, h
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------- energy
 # Energy per token of the sparse forward and of the dense torch FFN, from the
 # GPU's own power telemetry (amdsmi): each is run back to back (no cache
@@ -555,6 +633,8 @@ def main(argv=None):
                     help="slots per tile instead of the workload's own (same inputs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-baseline", action="store_true")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the ELL / pure TwELL / hybrid comparison at C = 4..8")
     ap.add_argument("--no-energy", action="store_true",
                     help="skip the energy-per-token legs (amdsmi power telemetry)")
     ap.add_argument("--no-layers", action="store_true",
@@ -732,6 +812,12 @@ def main(argv=None):
                 large_inputs = lt
             result["layers"][name] = time_layer(lc, steps, min(args.warmup, 3), flush, dev, lt)
             del lt
+    if not args.no_formats:
+        result["formats"] = {}
+        for name in FORMAT_WORKLOADS:
+            log(f"[bench] formats on {name}")
+            result["formats"][name] = time_formats(CONFIGS[name], min(args.layer_steps, 10),
+                                                   flush, dev)
     if not args.no_conversions:
         log(f"[bench] conversions on {CONVERSION_WORKLOAD}")
         result["conversions"] = time_conversions(CONFIGS[CONVERSION_WORKLOAD], args.steps,
