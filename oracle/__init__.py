@@ -5,16 +5,20 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 """
 from .twell_oracle import (  # noqa: F401
     Ell,
+    Grads,
     Hybrid,
     bf16_bits_to_f32,
     ell_pack,
     ell_pack_textbook,
     ell_unpack,
+    ffn_backward,
+    ffn_backward_from_h,
     ffn_forward,
     ffn_forward_rows,
     ffn_hidden,
     pack,
     pack_reference,
+    sampled_dots,
     spmm,
     tile_counts,
     to_csr,
