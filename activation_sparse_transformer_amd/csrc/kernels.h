@@ -219,4 +219,39 @@ hipError_t launch_ell_spmm_sparse(const Geometry& g, int elem_bytes, const void*
                                   const uint16_t* cols, const uint16_t* cnt, const DenseSkip& skip,
                                   const void* w_down, void* y, hipStream_t s);
 
+// The layer's backward pass from the stored hybrid h (dz at h's non-zeros,
+// per-neuron weight and bias sums in row order, dx by the hybrid product).
+struct BwdHybrid {
+  const void* vals;
+  const uint8_t* idx;
+  const uint8_t* cnt;
+  const int32_t* dense_rows;
+  const void* dense_values;
+  const int32_t* n_dense;
+  int64_t cap;
+};
+struct BwdWorkspace {
+  void* dz_vals;                // [N][nt][C] dtype
+  void* dz_dense;               // [min(cap, N)][d_ff] dtype
+  unsigned long long* bits;     // [d_ff][ceil(N / 64)] (neuron, row) bitmap
+  int32_t* lpre;                // [d_ff][ceil(N / 64)] set bits before each word
+  int32_t* ncount;              // [d_ff] entries per neuron
+  int32_t* offsets;             // [d_ff + 1] first entry of each neuron
+  int32_t* ent_row;             // [entries] row of each entry, by neuron then row
+  float2* ent_hz;               // [entries] (h, dz) of each entry
+  float* part;                  // the entry area, reused for the fallback's partial sums
+  int64_t part_elems;
+  float* skinny;                // skinny_ws_bytes(g) or nullptr
+  size_t bytes;                 // total workspace bytes
+};
+// Entries the column lists may hold: every TwELL slot and every element of
+// the stored dense rows.
+int64_t bwd_max_entries(const Geometry& g, int64_t dense_cap);
+// Parts of a workspace at `ws` (nullptr: sizes only, in .bytes).
+BwdWorkspace bwd_carve(const Geometry& g, int elem_bytes, int64_t dense_cap, void* ws);
+hipError_t launch_backward(const Geometry& g, int elem_bytes, const BwdHybrid& hy, const void* x,
+                           const void* w_up_t, const void* w_down, const void* dy,
+                           const BwdWorkspace& w, void* dx, float* dw_up_t, float* db,
+                           float* dw_down, hipStream_t s);
+
 }  // namespace twell

@@ -487,3 +487,53 @@ TWELL_EXPORT int ell_spmm(const twell_shape* shape, const twell_ell* in, const v
                                   static_cast<const float*>(w_down), static_cast<float*>(y), st));
   return TWELL_OK;
 }
+
+// ------------------------------------------------------------------ backward
+namespace twell {
+namespace {
+
+// The backward's shape rules on top of check_shape: every entry's place fits
+// an int32.
+int check_backward_shape(const twell_shape* s, int64_t dense_capacity) {
+  int rc = check_shape(s, true);
+  if (rc != TWELL_OK) return rc;
+  if (dense_capacity < 0) return TWELL_ERR_INVALID_ARG;
+  if (bwd_max_entries(geometry(s), dense_capacity) > INT32_MAX) return TWELL_ERR_UNSUPPORTED;
+  return TWELL_OK;
+}
+
+}  // namespace
+}  // namespace twell
+
+TWELL_EXPORT size_t ffn_sparse_backward_workspace_size(const twell_shape* shape,
+                                                       int64_t dense_capacity) {
+  if (check_backward_shape(shape, dense_capacity) != TWELL_OK) return 0;
+  return bwd_carve(geometry(shape), elem_bytes(shape->dtype), dense_capacity, nullptr).bytes;
+}
+
+TWELL_EXPORT int ffn_sparse_backward(const twell_shape* shape, const void* x, const void* w_up_t,
+                                     const void* w_down, const twell_hybrid* h, const void* dy,
+                                     void* dx, float* dw_up_t, float* db_up, float* dw_down,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_shape(shape, true);
+  if (rc != TWELL_OK) return rc;
+  const Geometry g = geometry(shape);
+  if ((rc = check_hybrid(h, g.n_rows)) != TWELL_OK) return rc;
+  if ((rc = check_backward_shape(shape, h->dense_capacity)) != TWELL_OK) return rc;
+  if (dw_up_t == nullptr || db_up == nullptr || dw_down == nullptr || workspace == nullptr)
+    return TWELL_ERR_INVALID_ARG;
+  if (g.n_rows > 0 &&
+      (x == nullptr || w_up_t == nullptr || w_down == nullptr || dy == nullptr || dx == nullptr))
+    return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_up_t) || !aligned16(w_down) || !aligned16(dy) ||
+      !aligned16(dx) || !aligned16(dw_up_t) || !aligned16(db_up) || !aligned16(dw_down) ||
+      !aligned16(workspace))
+    return TWELL_ERR_INVALID_ARG;
+  const int eb = elem_bytes(shape->dtype);
+  const BwdWorkspace w = bwd_carve(g, eb, h->dense_capacity, workspace);
+  if (workspace_bytes < w.bytes) return TWELL_ERR_WORKSPACE;
+  const BwdHybrid hy{h->values,       h->indices, h->counts,         h->dense_rows,
+                     h->dense_values, h->n_dense, h->dense_capacity};
+  return hip_status(launch_backward(g, eb, hy, x, w_up_t, w_down, dy, w, dx, dw_up_t, db_up,
+                                    dw_down, static_cast<hipStream_t>(stream)));
+}

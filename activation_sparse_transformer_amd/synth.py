@@ -21,8 +21,8 @@ b0 = -1.645 / -2.326 / -1.282 gives the stated ~5% / ~1% / ~10% active units
 only under that reading.
 
 Random stream layout (fixed, independent of thread count): one
-``SeedSequence(seed)`` spawns five children [x, token-scale, W_up, bias-noise,
-W_down]; each tensor's child spawns one grandchild per block of
+``SeedSequence(seed)`` spawns six children [x, token-scale, W_up, bias-noise,
+W_down, dy] (dy: the upstream gradient of the backward pass, ~N(0, 1)); each tensor's child spawns one grandchild per block of
 ``CHUNK_ROWS`` rows, and each block is drawn with
 ``Generator(PCG64(grandchild)).standard_normal(..., dtype=float32)`` in
 row-major order.  Blocks are drawn on a thread pool.
@@ -150,4 +150,11 @@ def make_inputs(cfg: FfnConfig) -> dict[str, torch.Tensor]:
         "b_up": torch.from_numpy(b.astype(np.float32)),
         "w_down": _cast(w_down, cfg.dtype),
     }
+
+
+def make_grad(cfg: FfnConfig) -> torch.Tensor:
+    """Return dy [N, d_model] ~ N(0, 1) in the storage dtype (CPU): the
+    upstream gradient of the layer's output, from the sixth child stream."""
+    s_dy = SeedSequence(cfg.seed).spawn(6)[5]
+    return _cast(draw_normal(s_dy, (cfg.n_rows, cfg.d_model)), cfg.dtype)
 

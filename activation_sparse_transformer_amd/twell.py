@@ -32,6 +32,7 @@ EXPORTS = (
     "twell_version", "twell_status_string", "ffn_sparse_workspace_size", "ffn_sparse_forward",
     "ffn_sparse_forward_events", "twell_pack_workspace_size", "twell_pack", "twell_pack_noalloc",
     "twell_unpack", "twell_spmm", "ell_pack_workspace_size", "ell_pack", "ell_unpack", "ell_spmm",
+    "ffn_sparse_backward_workspace_size", "ffn_sparse_backward",
 )
 
 
@@ -97,6 +98,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ell_pack.argtypes, lib.ell_pack.restype = [S, P, E, P, sz, P, P], I
     lib.ell_unpack.argtypes, lib.ell_unpack.restype = [S, E, P, P], I
     lib.ell_spmm.argtypes, lib.ell_spmm.restype = [S, E, P, P, P], I
+    i64 = ctypes.c_int64
+    lib.ffn_sparse_backward_workspace_size.argtypes = [S, i64]
+    lib.ffn_sparse_backward_workspace_size.restype = sz
+    lib.ffn_sparse_backward.argtypes = [S, P, P, P, H, P, P, P, P, P, P, sz, P]
+    lib.ffn_sparse_backward.restype = I
     _lib = lib
     return lib
 
@@ -476,3 +482,59 @@ def ell_spmm(e: Ell, w_down: torch.Tensor, out: Optional[torch.Tensor] = None) -
     _check(load().ell_spmm(ctypes.byref(shape), ctypes.byref(es), _ptr(w_down), _ptr(out),
                            _stream(dev)), "ell_spmm")
     return out
+
+
+# ------------------------------------------------------------------ backward
+def backward_workspace_bytes(shape: Shape, dense_capacity: int) -> int:
+    return int(load().ffn_sparse_backward_workspace_size(ctypes.byref(shape), dense_capacity))
+
+
+@dataclasses.dataclass
+class Grads:
+    """Everything ffn_sparse_backward writes."""
+
+    dx: torch.Tensor       # [N, d_model] dtype
+    dw_up_t: torch.Tensor  # [d_ff, d_model] float32
+    db_up: torch.Tensor    # [d_ff] float32
+    dw_down: torch.Tensor  # [d_ff, d_model] float32
+
+
+def ffn_sparse_backward(x: torch.Tensor, w_up_t: torch.Tensor, w_down: torch.Tensor,
+                        hy: Hybrid, dy: torch.Tensor, *, out: Optional[Grads] = None,
+                        workspace: Optional[torch.Tensor] = None) -> Grads:
+    """Gradients of sum(y * dy) for y = ReLU(x @ w_up_t.T + b_up) @ w_down from
+    the stored hybrid h of the forward pass: dx, dW_up^T, db_up, dW_down.
+
+    x, dy [N, d_model]; w_up_t, w_down [d_ff, d_model]; all in h's dtype.
+    Weight and bias gradients are float32.  Asynchronous like the forward."""
+    dev = x.device
+    n, dm = x.shape
+    dt = x.dtype
+    hy.validate(dev)
+    _need(x, "x", dev, hy.dtype, (hy.n_rows, dm))
+    _need(dy, "dy", dev, dt, (n, dm))
+    _need(w_up_t, "w_up_t", dev, dt, (hy.d_ff, dm))
+    _need(w_down, "w_down", dev, dt, (hy.d_ff, dm))
+    shape = make_shape(n, dm, hy.d_ff, hy.tile, hy.capacity, dt)
+    if out is None:
+        out = Grads(torch.empty((n, dm), dtype=dt, device=dev),
+                    torch.empty((hy.d_ff, dm), dtype=torch.float32, device=dev),
+                    torch.empty((hy.d_ff,), dtype=torch.float32, device=dev),
+                    torch.empty((hy.d_ff, dm), dtype=torch.float32, device=dev))
+    _need(out.dx, "dx", dev, dt, (n, dm))
+    _need(out.dw_up_t, "dw_up_t", dev, torch.float32, (hy.d_ff, dm))
+    _need(out.db_up, "db_up", dev, torch.float32, (hy.d_ff,))
+    _need(out.dw_down, "dw_down", dev, torch.float32, (hy.d_ff, dm))
+    if workspace is None:
+        ws = backward_workspace_bytes(shape, hy.dense_capacity)
+        if ws == 0:
+            raise TwellError(TWELL_ERR_UNSUPPORTED, "ffn_sparse_backward_workspace_size")
+        workspace = torch.empty((ws,), dtype=torch.uint8, device=dev)
+    hs = hy.struct()
+    code = load().ffn_sparse_backward(
+        ctypes.byref(shape), _ptr(x), _ptr(w_up_t), _ptr(w_down), ctypes.byref(hs), _ptr(dy),
+        _ptr(out.dx), _ptr(out.dw_up_t), _ptr(out.db_up), _ptr(out.dw_down), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    _check(code, "ffn_sparse_backward")
+    return out
+

@@ -314,6 +314,52 @@ int ell_unpack(const twell_shape* shape, const twell_ell* in, void* h, void* str
 int ell_spmm(const twell_shape* shape, const twell_ell* in, const void* w_down, void* y,
              void* stream);
 
+/* ---- The layer's backward pass.  "Sparser, Faster, Lighter Transformer
+ * Language Models (Sakana AI + NVIDIA)" (TL;DR and Figure 1 description)
+ * carries the sparse format into training as well as inference; "Nvidia and
+ * Sakana make LLMs 30% faster by doing less math", section "More speed, less
+ * power, zero quality loss", reports the training-side speed and peak-memory
+ * gains.  The pages do not write the gradients out; they follow from the
+ * forward y = ReLU(x W_up + b_up) W_down by the chain rule, with the ReLU's
+ * derivative read from the stored h (1 where h != 0, 0 elsewhere; at a
+ * pre-activation of exactly 0 the derivative is taken as 0, the usual
+ * convention). */
+
+/* Bytes of device workspace ffn_sparse_backward needs for this shape and a
+ * hybrid h with `dense_capacity` dense-row slots (0 for an invalid shape or
+ * when the column lists would hold more than 2^31 - 1 entries): dz in h's
+ * slots and in its dense rows, a (neuron, row) bitmap of h's non-zeros, and
+ * one (row, h, dz) entry per TwELL slot and per stored dense element. */
+size_t ffn_sparse_backward_workspace_size(const twell_shape* shape, int64_t dense_capacity);
+
+/* Gradients of L = sum(y * dy) for y = ReLU(x W_up + b_up) W_down, from the
+ * stored hidden activations h (the hybrid that ffn_sparse_forward or
+ * twell_pack wrote for the same x, weights and shape):
+ *   dz      = dy W_down^T at the non-zeros of h (0 elsewhere), rounded to
+ *             the storage type;
+ *   dw_down = h^T dy                  [d_ff][d_model] float32
+ *   dw_up_t = dz^T x (W_up transposed) [d_ff][d_model] float32
+ *   db_up   = column sums of dz        [d_ff] float32
+ *   dx      = dz W_up (= dz w_up_t)    [n_rows][d_model] dtype
+ * Each weight and bias gradient element is one float32 sum over the rows
+ * where h is non-zero, in ascending row order; the results do not depend on
+ * scheduling and are written, not added to (the caller accumulates over
+ * micro-batches).  dx is the hybrid product of twell_spmm with dz's values
+ * in h's slots and rows.  A row listed among the stored dense rows is read
+ * from dense_values only; after a TWELL_ERR_DENSE_CAPACITY forward the rows
+ * past dense_capacity hold no non-zero, so they contribute nothing and get
+ * dx = 0.
+ * Arguments: shape (host pointer; the forward's shape); x, w_up_t, w_down,
+ * dy [n_rows][d_model] inputs in dtype; h (host pointer to device pointers)
+ * the stored activations; dx, dw_up_t, db_up, dw_down outputs; workspace of
+ * at least ffn_sparse_backward_workspace_size(shape, h->dense_capacity)
+ * bytes, never NULL, contents undefined on entry and exit.  n_rows == 0
+ * writes zero weight and bias gradients. */
+int ffn_sparse_backward(const twell_shape* shape, const void* x, const void* w_up_t,
+                        const void* w_down, const twell_hybrid* h, const void* dy, void* dx,
+                        float* dw_up_t, float* db_up, float* dw_down, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -142,3 +142,55 @@ def test_noalloc_pack_rejects_shapes_beyond_its_scratch(lib):
     assert lib.twell_pack_noalloc(ctypes.byref(s), a, ctypes.byref(h), None, None) == \
         twell.TWELL_ERR_SCRATCH_LIMIT
     assert "scratch" in twell.status_string(twell.TWELL_ERR_SCRATCH_LIMIT)
+
+
+def _align(v):
+    return (v + 255) // 256 * 256
+
+
+def test_backward_workspace_size(lib):
+    """dz in h's slots and dense rows, the (neuron, row) bitmap and its word
+    prefixes, per-neuron counts and offsets, one (row, h, dz) entry per slot
+    and per stored dense element, and (at most 64 rows) the fallback's split-K
+    partial sums; each part 256-byte aligned."""
+    n, dm, dff, T, C, cap = 4096, 2048, 8192, 128, 4, 512
+    s = twell.make_shape(n, dm, dff, T, C, torch.bfloat16)
+    slots = n * (dff // T) * C
+    words = dff * ((n + 63) // 64)
+    ents = slots + cap * dff
+    want = (_align(slots * 2) + _align(cap * dff * 2) + _align(words * 8) + _align(words * 4) +
+            _align(dff * 4) + _align((dff + 1) * 4) + _align(ents * 4) + _align(ents * 8))
+    assert twell.backward_workspace_bytes(s, cap) == want
+    # dense capacity past n_rows counts as n_rows
+    assert twell.backward_workspace_bytes(s, 10 * n) == twell.backward_workspace_bytes(s, n)
+    # 40 rows: the fallback's split-K partial sums fp32 [32 slices][64 rows][768]
+    small = twell.make_shape(40, 136, 768, 128, 4, torch.bfloat16)
+    slots, words = 40 * 6 * 4, 768
+    want = (_align(slots * 2) + _align(words * 8) + _align(words * 4) + _align(768 * 4) +
+            _align(769 * 4) + _align(slots * 4) + _align(slots * 8) + 32 * 64 * 768 * 4)
+    assert twell.backward_workspace_bytes(small, 0) == want
+    # invalid: negative capacity, a bad shape, more entries than an int32 can place
+    assert twell.backward_workspace_bytes(s, -1) == 0
+    assert twell.backward_workspace_bytes(twell.make_shape(16, 2048, 8192, 100, 4,
+                                                          torch.bfloat16), 0) == 0
+    huge = twell.make_shape(1 << 20, 8, 65536, 256, 255, torch.bfloat16)  # 2^20 * 256 * 255 slots
+    assert twell.backward_workspace_bytes(huge, 0) == 0
+
+
+@no_gpu_only
+def test_backward_host_checks(lib):
+    s = twell.Shape(64, 128, 512, 128, 4, 1, 0)
+    a = 4096
+    h = twell.HybridStruct(a, a, a, None, None, a, 0)
+    ws = lib.ffn_sparse_backward_workspace_size(ctypes.byref(s), 0)
+    call = lambda **kw: lib.ffn_sparse_backward(
+        ctypes.byref(s), kw.get("x", a), a, a, ctypes.byref(h), a, kw.get("dx", a),
+        kw.get("dwu", a), a, a, kw.get("ws", a), kw.get("wsb", ws), None)
+    assert call(wsb=ws - 1) == twell.TWELL_ERR_WORKSPACE
+    assert call(ws=None) == twell.TWELL_ERR_INVALID_ARG
+    assert call(dwu=None) == twell.TWELL_ERR_INVALID_ARG
+    assert call(x=None) == twell.TWELL_ERR_INVALID_ARG
+    assert call(dx=a + 4) == twell.TWELL_ERR_INVALID_ARG  # misaligned
+    bad = twell.HybridStruct(a, a, a, None, None, a, -1)
+    assert lib.ffn_sparse_backward(ctypes.byref(s), a, a, a, ctypes.byref(bad), a, a, a, a, a, a,
+                                   ws, None) == twell.TWELL_ERR_INVALID_ARG
