@@ -231,19 +231,31 @@ struct BwdHybrid {
   int64_t cap;
 };
 struct BwdWorkspace {
+  unsigned long long* bits;     // [d_ff][ceil(N / 64)] (neuron, row) bitmap
+  uint8_t* row_flag;            // [N] 1 for a stored dense row
+  int64_t zero_words;           // 4-byte words of bits + row_flag, cleared together
   void* dz_vals;                // [N][nt][C] dtype
   void* dz_dense;               // [min(cap, N)][d_ff] dtype
-  unsigned long long* bits;     // [d_ff][ceil(N / 64)] (neuron, row) bitmap
   int32_t* lpre;                // [d_ff][ceil(N / 64)] set bits before each word
   int32_t* ncount;              // [d_ff] entries per neuron
   int32_t* offsets;             // [d_ff + 1] first entry of each neuron
-  int32_t* ent_row;             // [entries] row of each entry, by neuron then row
-  float2* ent_hz;               // [entries] (h, dz) of each entry
+  int4* ents;                   // [entries] {row, h as f32 bits, slot, 0}, by neuron then row
+  float* part_dz;               // [entries][S] partial dots of dz per column slice
   float* part;                  // the entry area, reused for the fallback's partial sums
   int64_t part_elems;
   float* skinny;                // skinny_ws_bytes(g) or nullptr
   size_t bytes;                 // total workspace bytes
 };
+// Column slices of the backward's per-neuron passes: S slices of sw columns,
+// P lanes and nvl 16-byte vectors per lane per slice (nvl = 0: unsupported).
+struct SlicePlan {
+  int S, sw, P, nvl;
+};
+SlicePlan bwd_slice_plan(int d_model, int elem_bytes);
+// Whether the backward covers this d_model (a slice of at most 64 lanes x 4
+// vectors x 16 bytes: 16384 bf16 or 8192 fp32 columns when d_model splits in
+// 8 slices, 2048 / 1024 otherwise).
+bool bwd_supported(const Geometry& g, int elem_bytes);
 // Entries the column lists may hold: every TwELL slot and every element of
 // the stored dense rows.
 int64_t bwd_max_entries(const Geometry& g, int64_t dense_cap);

@@ -499,6 +499,7 @@ int check_backward_shape(const twell_shape* s, int64_t dense_capacity) {
   if (rc != TWELL_OK) return rc;
   if (dense_capacity < 0) return TWELL_ERR_INVALID_ARG;
   if (bwd_max_entries(geometry(s), dense_capacity) > INT32_MAX) return TWELL_ERR_UNSUPPORTED;
+  if (!bwd_supported(geometry(s), elem_bytes(s->dtype))) return TWELL_ERR_UNSUPPORTED;
   return TWELL_OK;
 }
 

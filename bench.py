@@ -499,6 +499,107 @@ def measure_energy(tokens_per_call: int, fns: dict, idle_w, seconds: float = ENE
             pass
 
 
+# The layer's training step.  The sparse backward (ffn_sparse_backward) reads
+# the hybrid h that the sparse forward stored; the dense baseline is what
+# autograd runs for the same bf16 layer with h stored dense: dz = (dy W_down^T)
+# masked by h > 0, dW_down = h^T dy, dW_up^T = dz^T x, db = column sums of dz,
+# dx = dz W_up, four hipBLASLt GEMMs.  The sparse path writes its weight
+# gradients in float32, the dense one in bf16.  Both are timed alone and as a
+# whole step (forward + backward), cold cache, and the activations each
+# forward keeps for the backward are counted.
+BACKWARD_WORKLOADS = ("ffn_1b_bf16", "decode_bf16")
+
+
+def dense_backward(d, h, dy):
+    def run():
+        dz = torch.matmul(dy, d["w_down"].t()) * (h > 0)
+        dw_down = torch.matmul(h.t(), dy)
+        dw_up_t = torch.matmul(dz.t(), d["x"])
+        db = dz.sum(dim=0, dtype=torch.float32)
+        dx = torch.matmul(dz, d["w_up_t"])
+        return dx, dw_up_t, db, dw_down
+    return run
+
+
+def hybrid_bytes(hy: twell.Hybrid, n_dense: int) -> int:
+    """Bytes of the stored hybrid h the backward reads: slots, indices,
+    counts and the stored dense rows with their row numbers."""
+    e = hy.values.element_size()
+    return (hy.values.numel() * e + hy.indices.numel() + hy.counts.numel() +
+            n_dense * (hy.d_ff * e + 4) + 4)
+
+
+def time_backward(cfg, steps, warmup, flush, dev, t=None):
+    from activation_sparse_transformer_amd.synth import make_grad
+    t = make_inputs(cfg) if t is None else t
+    d = {k: v.to(dev) for k, v in t.items()}
+    dy = make_grad(cfg).to(dev)
+    bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
+                                 cfg.torch_dtype, dev)
+    fwd = lambda: twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"],
+                                           cfg.tile, cfg.capacity, out=bufs)
+    fwd()
+    torch.cuda.synchronize()
+    if int(bufs.status.item()) != twell.TWELL_OK:
+        raise RuntimeError(f"{cfg.name} forward reported an error status")
+    hy = bufs.hybrid
+    n_dense = hy.n_dense_host()
+    shape = twell.make_shape(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
+                             cfg.torch_dtype)
+    ws = torch.empty((twell.backward_workspace_bytes(shape, hy.dense_capacity),),
+                     dtype=torch.uint8, device=dev)
+    grads = twell.Grads(torch.empty_like(d["x"]),
+                        torch.empty((cfg.d_ff, cfg.d_model), dtype=torch.float32, device=dev),
+                        torch.empty((cfg.d_ff,), dtype=torch.float32, device=dev),
+                        torch.empty((cfg.d_ff, cfg.d_model), dtype=torch.float32, device=dev))
+    bwd = lambda: twell.ffn_sparse_backward(d["x"], d["w_up_t"], d["w_down"], hy, dy,
+                                            out=grads, workspace=ws)
+    sb = _timed_calls(bwd, steps, warmup, flush)
+    sstep = _timed_calls(lambda: (fwd(), bwd()), steps, warmup, flush)
+    nnz = int((hy.counts.to(torch.int64)).sum().item()) + int(
+        (hy.dense_values[:min(n_dense, hy.dense_capacity)] != 0).sum().item())
+    stored = hybrid_bytes(hy, n_dense)
+    ws_bytes = ws.numel()
+    del grads, ws, bufs
+    torch.cuda.empty_cache()
+    dense_fwd = dense_ffn(d)
+    b16 = d["b_up"].to(d["x"].dtype)
+    h = torch.relu(torch.nn.functional.linear(d["x"], d["w_up_t"], b16))
+    db_run = dense_backward(d, h, dy)
+
+    def dense_step():
+        hh = torch.relu(torch.nn.functional.linear(d["x"], d["w_up_t"], b16))
+        torch.matmul(hh, d["w_down"])
+        dense_backward(d, hh, dy)()
+
+    db_ms = _timed_calls(db_run, steps, warmup, flush)
+    dstep = _timed_calls(dense_step, steps, warmup, flush)
+    del dense_fwd, h, d, dy
+    torch.cuda.empty_cache()
+    ms, dms, st, dst = median(sb), median(db_ms), median(sstep), median(dstep)
+    e = cfg.elem_bytes
+    N, dm, dff = cfg.n_rows, cfg.d_model, cfg.d_ff
+    return {
+        "workload": cfg.name, "n_rows": N, "d_model": dm, "d_ff": dff, "tile": cfg.tile,
+        "capacity": cfg.capacity, "steps": steps, "n_dense": n_dense, "nonzeros_h": nnz,
+        "sparse_backward_ms": ms, "sparse_backward_p10": percentile(sb, 10),
+        "sparse_backward_p90": percentile(sb, 90),
+        "dense_backward_ms": dms, "dense_backward_p10": percentile(db_ms, 10),
+        "dense_backward_p90": percentile(db_ms, 90),
+        "speedup_backward": dms / ms,
+        "sparse_step_ms": st, "dense_step_ms": dst, "speedup_step": dst / st,
+        "training_tokens_per_s_sparse": N / (st * 1e-3),
+        "training_tokens_per_s_dense": N / (dst * 1e-3),
+        # 2 flops per product: dz, dW_down, dW_up, dx at every non-zero of h
+        "sparse_backward_algorithmic_tflops": 8.0 * nnz * dm / (ms * 1e-3) / 1e12,
+        "dense_backward_tflops": 8.0 * N * dff * dm / (dms * 1e-3) / 1e12,
+        "stored_activation_bytes_sparse": stored,
+        "stored_activation_bytes_dense": N * dff * e,
+        "sparse_backward_workspace_bytes": ws_bytes,
+        "weight_grad_dtype": {"sparse": "f32", "dense": cfg.dtype},
+    }
+
+
 def dense_ffn(d):
     """The layer as a plain dense FFN through torch (hipBLASLt)."""
     b16 = d["b_up"].to(d["x"].dtype)
@@ -639,6 +740,8 @@ def main(argv=None):
                     help="skip the energy-per-token legs (amdsmi power telemetry)")
     ap.add_argument("--no-layers", action="store_true",
                     help="skip the other workloads timed beside the headline one")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training step (sparse backward against dense autograd)")
     ap.add_argument("--no-conversions", action="store_true",
                     help="skip twell_pack / twell_unpack on the 16384-token layer's h")
     args = ap.parse_args(argv)
@@ -818,6 +921,13 @@ def main(argv=None):
             log(f"[bench] formats on {name}")
             result["formats"][name] = time_formats(CONFIGS[name], min(args.layer_steps, 10),
                                                    flush, dev)
+    if not args.no_backward:
+        result["backward"] = {}
+        for name in BACKWARD_WORKLOADS:
+            log(f"[bench] backward on {name}")
+            result["backward"][name] = time_backward(CONFIGS[name], min(args.layer_steps, 10),
+                                                     min(args.warmup, 3), flush, dev,
+                                                     t if name == cfg.name else None)
     if not args.no_conversions:
         log(f"[bench] conversions on {CONVERSION_WORKLOAD}")
         result["conversions"] = time_conversions(CONFIGS[CONVERSION_WORKLOAD], args.steps,

@@ -327,9 +327,11 @@ int ell_spmm(const twell_shape* shape, const twell_ell* in, const void* w_down, 
 
 /* Bytes of device workspace ffn_sparse_backward needs for this shape and a
  * hybrid h with `dense_capacity` dense-row slots (0 for an invalid shape or
- * when the column lists would hold more than 2^31 - 1 entries): dz in h's
- * slots and in its dense rows, a (neuron, row) bitmap of h's non-zeros, and
- * one (row, h, dz) entry per TwELL slot and per stored dense element. */
+ * when the per-neuron lists would hold more than 2^31 - 1 entries or d_model
+ * is past the backward's limit): dz in
+ * h's slots and in its dense rows, a (neuron, row) bitmap of h's non-zeros
+ * with its word prefixes, one flag per row, and one 16-byte entry per TwELL
+ * slot and per stored dense element. */
 size_t ffn_sparse_backward_workspace_size(const twell_shape* shape, int64_t dense_capacity);
 
 /* Gradients of L = sum(y * dy) for y = ReLU(x W_up + b_up) W_down, from the
@@ -349,6 +351,8 @@ size_t ffn_sparse_backward_workspace_size(const twell_shape* shape, int64_t dens
  * from dense_values only; after a TWELL_ERR_DENSE_CAPACITY forward the rows
  * past dense_capacity hold no non-zero, so they contribute nothing and get
  * dx = 0.
+ * d_model is at most 16384 (bf16) or 8192 (float32), else
+ * TWELL_ERR_UNSUPPORTED.
  * Arguments: shape (host pointer; the forward's shape); x, w_up_t, w_down,
  * dy [n_rows][d_model] inputs in dtype; h (host pointer to device pointers)
  * the stored activations; dx, dw_up_t, db_up, dw_down outputs; workspace of

@@ -149,25 +149,27 @@ def _align(v):
 
 
 def test_backward_workspace_size(lib):
-    """dz in h's slots and dense rows, the (neuron, row) bitmap and its word
-    prefixes, per-neuron counts and offsets, one (row, h, dz) entry per slot
-    and per stored dense element, and (at most 64 rows) the fallback's split-K
-    partial sums; each part 256-byte aligned."""
+    """The (neuron, row) bitmap and one row flag per token, dz in h's slots
+    and dense rows, the bitmap's word prefixes, per-neuron counts and offsets,
+    one 16-byte entry per slot and per stored dense element, and (at most 64
+    rows) the fallback's split-K partial sums; each part 256-byte aligned."""
     n, dm, dff, T, C, cap = 4096, 2048, 8192, 128, 4, 512
     s = twell.make_shape(n, dm, dff, T, C, torch.bfloat16)
     slots = n * (dff // T) * C
     words = dff * ((n + 63) // 64)
     ents = slots + cap * dff
-    want = (_align(slots * 2) + _align(cap * dff * 2) + _align(words * 8) + _align(words * 4) +
-            _align(dff * 4) + _align((dff + 1) * 4) + _align(ents * 4) + _align(ents * 8))
+    want = (_align(words * 8) + _align(n) + _align(slots * 2) + _align(cap * dff * 2) +
+            _align(words * 4) + _align(dff * 4) + _align((dff + 1) * 4) + _align(ents * 16) +
+            _align(8 * ents * 4))  # partial dots of dz, one per column slice (8 XCDs)
     assert twell.backward_workspace_bytes(s, cap) == want
     # dense capacity past n_rows counts as n_rows
     assert twell.backward_workspace_bytes(s, 10 * n) == twell.backward_workspace_bytes(s, n)
     # 40 rows: the fallback's split-K partial sums fp32 [32 slices][64 rows][768]
     small = twell.make_shape(40, 136, 768, 128, 4, torch.bfloat16)
     slots, words = 40 * 6 * 4, 768
-    want = (_align(slots * 2) + _align(words * 8) + _align(words * 4) + _align(768 * 4) +
-            _align(769 * 4) + _align(slots * 4) + _align(slots * 8) + 32 * 64 * 768 * 4)
+    want = (_align(words * 8) + _align(40) + _align(slots * 2) + _align(words * 4) +
+            _align(768 * 4) + _align(769 * 4) + _align(slots * 16) + _align(slots * 4) +
+            32 * 64 * 768 * 4)  # d_model 136 is one column slice
     assert twell.backward_workspace_bytes(small, 0) == want
     # invalid: negative capacity, a bad shape, more entries than an int32 can place
     assert twell.backward_workspace_bytes(s, -1) == 0

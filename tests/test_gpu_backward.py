@@ -68,6 +68,10 @@ def check(g: twell.Grads, ref: oracle.Grads, tol):
     (500, 512, 2048, 256, 8, "bf16", -1.645, 0.5),
     (1000, 384, 1536, 128, 6, "fp32", -1.645, 0.5),
     (129, 1024, 512, 128, 16, "bf16", -2.326, 0.0),
+    # d_model past one pass of the per-neuron kernel: column chunks, ragged
+    (100, 2304, 512, 64, 4, "fp32", -1.645, 0.5),
+    (70, 4352, 512, 128, 8, "bf16", -1.645, 0.5),
+    (90, 4096, 1024, 128, 4, "bf16", -2.326, 0.5),
 ])
 def test_backward_matches_oracle(n, dm, dff, T, C, dtype, b0, tsv):
     say(f"backward {dtype} n={n} dm={dm} dff={dff} T={T} C={C}")
