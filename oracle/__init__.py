@@ -16,6 +16,8 @@ from .twell_oracle import (  # noqa: F401
     ffn_forward,
     ffn_forward_rows,
     ffn_hidden,
+    gated_ffn_forward,
+    gated_ffn_hidden,
     pack,
     pack_reference,
     sampled_dots,

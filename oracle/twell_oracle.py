@@ -344,6 +344,31 @@ def ell_unpack(e: Ell) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# ReLU-gated FFN (GLU form).  The pages describe only the non-gated layer; the
+# gated form is this oracle's extension, for LLaMA-style FFNs [repo "The
+# Repo's Two Jobs": a sparse LLaMA model], with its sparsity taken from the
+# ReLU of the gate exactly as the plain layer takes it from its ReLU [blog
+# "The Challenge of Sparsity Ignored by GPUs"].
+# --------------------------------------------------------------------------
+def gated_ffn_hidden(x, w_gate_t, b_gate, w_up_t, b_up) -> np.ndarray:
+    """h = ReLU(x W_gate + b_gate) * (x W_up + b_up), elementwise, in float64.
+
+    Both weights are stored transposed, [d_ff, d_model].  h is zero wherever
+    the gate's pre-activation is <= 0, whatever the up branch holds.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    zg = x @ np.asarray(w_gate_t, dtype=np.float64).T + np.asarray(b_gate, dtype=np.float64)[None, :]
+    zu = x @ np.asarray(w_up_t, dtype=np.float64).T + np.asarray(b_up, dtype=np.float64)[None, :]
+    return np.where(zg > 0.0, zg, 0.0) * zu
+
+
+def gated_ffn_forward(x, w_gate_t, b_gate, w_up_t, b_up, w_down):
+    """Return (h, y) of the gated FFN in float64: y = h @ W_down."""
+    h = gated_ffn_hidden(x, w_gate_t, b_gate, w_up_t, b_up)
+    return h, h @ np.asarray(w_down, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
 # Training step: the gradients of the layer [wiki TL;DR: inference and
 # training], [news "More speed, less power, zero quality loss"]
 # --------------------------------------------------------------------------
