@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libtwell.so")
 ARCH = "gfx950"
 
 SOURCES = ["twell_api.hip", "gemm_bf16.hip", "gemm_f32.hip", "route.hip", "spmm.hip", "skinny.hip",
-           "ell.hip", "backward.hip"]
+           "ell.hip", "backward.hip", "gate.hip"]
 
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",

@@ -266,4 +266,24 @@ hipError_t launch_backward(const Geometry& g, int elem_bytes, const BwdHybrid& h
                            const BwdWorkspace& w, void* dx, float* dw_up_t, float* db,
                            float* dw_down, hipStream_t s);
 
+// The ReLU-gated FFN's up branch on a packed and routed gate: each stored
+// non-zero g (TwELL slots of the sparse rows sparse_rows[0 .. *n_sparse),
+// non-zeros of the stored dense rows) becomes g * (x[n] . w_up_t[j] + b_up[j])
+// rounded to the storage type, in place.
+struct GateHybrid {
+  void* vals;
+  const uint8_t* idx;
+  const uint8_t* cnt;
+  const int32_t* dense_rows;
+  void* dense_values;
+  const int32_t* n_dense;
+  int64_t cap;
+  const int32_t* sparse_rows;
+  const int32_t* n_sparse;
+};
+// Whether launch_gate_up covers this shape (d_model up to 16 x 64 x 16 bytes).
+bool gate_supported(const Geometry& g, int elem_bytes);
+hipError_t launch_gate_up(const Geometry& g, int elem_bytes, const GateHybrid& hy, const void* x,
+                          const void* w_up_t, const float* b_up, hipStream_t s);
+
 }  // namespace twell

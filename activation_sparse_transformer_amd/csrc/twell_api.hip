@@ -197,10 +197,18 @@ namespace {
 // The forward pass; `ev`, when given, holds five events recorded on the
 // stream before step 1 and after each of steps 1-4 (which then run in
 // order on the stream).
+// The gated layer's up branch: step 1 then runs on the gate's weights (the
+// x, w_up_t, b_up arguments), and the up branch is applied at the gate's
+// non-zeros between steps 2 and 3.
+struct GateArgs {
+  const void* w_up_t;
+  const float* b_up;
+};
+
 int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, const float* b_up,
                  const void* w_down, void* y, const twell_hybrid* h_out, void* h_dense_debug,
                  void* workspace, size_t workspace_bytes, int32_t* d_status, void* stream,
-                 void* const* ev) {
+                 void* const* ev, const GateArgs* gate = nullptr) {
   int rc = check_shape(shape, true);
   if (rc != TWELL_OK) return rc;
   const Geometry g = geometry(shape);
@@ -240,11 +248,18 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
   // 2. route rows, build dense rows from the TwELL slots + spilled tiles; for
   // float32 batches of at most 64 rows (plain call) the build's sparse-row
   // workgroups also run step 3 for their rows
-  const bool build_spmm = ev == nullptr && g.n_rows > 0 && build_takes_spmm(g, eb);
+  const bool build_spmm = ev == nullptr && gate == nullptr && g.n_rows > 0 && build_takes_spmm(g, eb);
   const BuildSpmm bsp{w_down, y};
   if ((rc = route_and_materialize(g, eb, w, nullptr, h_out, d_status, st,
                                   build_spmm ? &bsp : nullptr)) != TWELL_OK)
     return rc;
+  if (gate != nullptr) {
+    // the gated layer: h = gate * (x W_up + b_up) at the gate's non-zeros
+    const GateHybrid gh{h_out->values,       h_out->indices, h_out->counts,
+                        h_out->dense_rows,   h_out->dense_values, h_out->n_dense,
+                        h_out->dense_capacity, w.route.sparse_rows, w.route.n_sparse};
+    TWELL_TRY(launch_gate_up(g, eb, gh, x, gate->w_up_t, gate->b_up, st));
+  }
   TWELL_TRY(mark(2));
   // 3. sparse down-projection of the TwELL rows and 4. dense fallback for the
   // dense rows, one after the other on the caller's stream (they write
@@ -288,6 +303,22 @@ int forward_impl(const twell_shape* shape, const void* x, const void* w_up_t, co
 
 }  // namespace
 }  // namespace twell
+
+TWELL_EXPORT int ffn_sparse_gated_forward(const twell_shape* shape, const void* x,
+                                          const void* w_gate_t, const float* b_gate,
+                                          const void* w_up_t, const float* b_up,
+                                          const void* w_down, void* y, const twell_hybrid* h_out,
+                                          void* workspace, size_t workspace_bytes,
+                                          int32_t* d_status, void* stream) {
+  const int rc = check_shape(shape, true);
+  if (rc != TWELL_OK) return rc;
+  if (shape->n_rows > 0 && (w_up_t == nullptr || b_up == nullptr)) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(w_up_t)) return TWELL_ERR_INVALID_ARG;
+  if (!gate_supported(geometry(shape), elem_bytes(shape->dtype))) return TWELL_ERR_UNSUPPORTED;
+  const GateArgs gate{w_up_t, b_up};
+  return forward_impl(shape, x, w_gate_t, b_gate, w_down, y, h_out, nullptr, workspace,
+                      workspace_bytes, d_status, stream, nullptr, &gate);
+}
 
 TWELL_EXPORT int ffn_sparse_forward(const twell_shape* shape, const void* x, const void* w_up_t,
                                     const float* b_up, const void* w_down, void* y,

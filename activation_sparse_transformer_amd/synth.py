@@ -21,8 +21,10 @@ b0 = -1.645 / -2.326 / -1.282 gives the stated ~5% / ~1% / ~10% active units
 only under that reading.
 
 Random stream layout (fixed, independent of thread count): one
-``SeedSequence(seed)`` spawns six children [x, token-scale, W_up, bias-noise,
-W_down, dy] (dy: the upstream gradient of the backward pass, ~N(0, 1)); each tensor's child spawns one grandchild per block of
+``SeedSequence(seed)`` spawns seven children [x, token-scale, W_up, bias-noise,
+W_down, dy, W_up of a gated layer's up branch] (dy: the upstream gradient of
+the backward pass, ~N(0, 1); the gated layer takes the plain recipe's W_up and
+b as its gate and draws its up branch ~N(0, 1/d_model), bias 0); each tensor's child spawns one grandchild per block of
 ``CHUNK_ROWS`` rows, and each block is drawn with
 ``Generator(PCG64(grandchild)).standard_normal(..., dtype=float32)`` in
 row-major order.  Blocks are drawn on a thread pool.
@@ -157,4 +159,16 @@ def make_grad(cfg: FfnConfig) -> torch.Tensor:
     upstream gradient of the layer's output, from the sixth child stream."""
     s_dy = SeedSequence(cfg.seed).spawn(6)[5]
     return _cast(draw_normal(s_dy, (cfg.n_rows, cfg.d_model)), cfg.dtype)
+
+
+def make_gated_inputs(cfg: FfnConfig) -> dict[str, torch.Tensor]:
+    """Inputs of the ReLU-gated layer: x, w_gate_t / b_gate (the plain
+    recipe's W_up and b, so the gate has the plain layer's sparsity), w_up_t
+    ~N(0, 1/d_model) from the seventh child stream, b_up = 0 (fp32), w_down."""
+    t = make_inputs(cfg)
+    s_up = SeedSequence(cfg.seed).spawn(7)[6]
+    w = draw_normal(s_up, (cfg.d_ff, cfg.d_model))
+    w *= np.float32(1.0 / math.sqrt(cfg.d_model))
+    return {"x": t["x"], "w_gate_t": t["w_up_t"], "b_gate": t["b_up"], "w_up_t": _cast(w, cfg.dtype),
+            "b_up": torch.zeros(cfg.d_ff, dtype=torch.float32), "w_down": t["w_down"]}
 

@@ -32,7 +32,7 @@ EXPORTS = (
     "twell_version", "twell_status_string", "ffn_sparse_workspace_size", "ffn_sparse_forward",
     "ffn_sparse_forward_events", "twell_pack_workspace_size", "twell_pack", "twell_pack_noalloc",
     "twell_unpack", "twell_spmm", "ell_pack_workspace_size", "ell_pack", "ell_unpack", "ell_spmm",
-    "ffn_sparse_backward_workspace_size", "ffn_sparse_backward",
+    "ffn_sparse_backward_workspace_size", "ffn_sparse_backward", "ffn_sparse_gated_forward",
 )
 
 
@@ -89,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ffn_sparse_forward.restype = I
     lib.ffn_sparse_forward_events.argtypes = [S, P, P, P, P, P, H, P, P, sz, P, P, P]
     lib.ffn_sparse_forward_events.restype = I
+    lib.ffn_sparse_gated_forward.argtypes = [S, P, P, P, P, P, P, P, H, P, sz, P, P]
+    lib.ffn_sparse_gated_forward.restype = I
     lib.twell_pack.argtypes, lib.twell_pack.restype = [S, P, H, P, sz, P, P], I
     lib.twell_pack_noalloc.argtypes, lib.twell_pack_noalloc.restype = [S, P, H, P, P], I
     lib.twell_unpack.argtypes, lib.twell_unpack.restype = [S, H, P, P], I
@@ -287,6 +289,35 @@ def ffn_sparse_forward(x: torch.Tensor, w_up_t: torch.Tensor, b_up: torch.Tensor
         arr = (ctypes.c_void_p * 5)(*[e.cuda_event for e in stage_events])
         code = load().ffn_sparse_forward_events(*args, arr)
     _check(code, "ffn_sparse_forward")
+    return out
+
+
+def ffn_sparse_gated_forward(x: torch.Tensor, w_gate_t: torch.Tensor, b_gate: torch.Tensor,
+                             w_up_t: torch.Tensor, b_up: torch.Tensor, w_down: torch.Tensor,
+                             tile: int, capacity: int, *, dense_capacity: Optional[int] = None,
+                             out: Optional[ForwardBuffers] = None) -> ForwardBuffers:
+    """y = (ReLU(x @ w_gate_t.T + b_gate) * (x @ w_up_t.T + b_up)) @ w_down with h
+    in hybrid TwELL form (stored where the gate is non-zero).  Same buffers as
+    ffn_sparse_forward (no debug h)."""
+    dev = x.device
+    n, dm = x.shape
+    dff = w_gate_t.shape[0]
+    dt = x.dtype
+    _need(x, "x", dev, dt)
+    for name, w in (("w_gate_t", w_gate_t), ("w_up_t", w_up_t), ("w_down", w_down)):
+        _need(w, name, dev, dt, (dff, dm))
+    _need(b_gate, "b_gate", dev, torch.float32, (dff,))
+    _need(b_up, "b_up", dev, torch.float32, (dff,))
+    if out is None:
+        out = forward_buffers(n, dm, dff, tile, capacity, dt, dev, dense_capacity)
+    shape = make_shape(n, dm, dff, tile, capacity, dt)
+    _need(out.y, "y", dev, dt, (n, dm))
+    out.hybrid.validate(dev)
+    hs = out.hybrid.struct()
+    _check(load().ffn_sparse_gated_forward(
+        ctypes.byref(shape), _ptr(x), _ptr(w_gate_t), _ptr(b_gate), _ptr(w_up_t), _ptr(b_up),
+        _ptr(w_down), _ptr(out.y), ctypes.byref(hs), _ptr(out.workspace), out.workspace.numel(),
+        _ptr(out.status), _stream(dev)), "ffn_sparse_gated_forward")
     return out
 
 

@@ -600,6 +600,50 @@ def time_backward(cfg, steps, warmup, flush, dev, t=None):
     }
 
 
+# The ReLU-gated layer (gate = the plain recipe's W_up and bias, up branch
+# ~N(0, 1/d_model)): the sparse gated forward against the same layer as three
+# dense bf16 GEMMs through torch, cold cache, plain calls.
+GATED_WORKLOADS = ("ffn_1b_bf16", "decode_bf16")
+
+
+def dense_gated_ffn(d):
+    bg = d["b_gate"].to(d["x"].dtype)
+    bu = d["b_up"].to(d["x"].dtype)
+
+    def run():
+        g = torch.relu(torch.nn.functional.linear(d["x"], d["w_gate_t"], bg))
+        u = torch.nn.functional.linear(d["x"], d["w_up_t"], bu)
+        return torch.matmul(g * u, d["w_down"])
+
+    return run
+
+
+def time_gated(cfg, steps, warmup, flush, dev):
+    from activation_sparse_transformer_amd.synth import make_gated_inputs
+    d = {k: v.to(dev) for k, v in make_gated_inputs(cfg).items()}
+    bufs = twell.forward_buffers(cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, cfg.capacity,
+                                 cfg.torch_dtype, dev)
+    fwd = lambda: twell.ffn_sparse_gated_forward(d["x"], d["w_gate_t"], d["b_gate"], d["w_up_t"],
+                                                 d["b_up"], d["w_down"], cfg.tile, cfg.capacity,
+                                                 out=bufs)
+    sp = _timed_calls(fwd, steps, warmup, flush)
+    if int(bufs.status.item()) != twell.TWELL_OK:
+        raise RuntimeError(f"{cfg.name} gated forward reported an error status")
+    n_dense = bufs.hybrid.n_dense_host()
+    del bufs
+    torch.cuda.empty_cache()
+    dn = _timed_calls(dense_gated_ffn(d), steps, warmup, flush)
+    del d
+    torch.cuda.empty_cache()
+    ms, dms = median(sp), median(dn)
+    return {"workload": cfg.name, "n_rows": cfg.n_rows, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+            "tile": cfg.tile, "capacity": cfg.capacity, "steps": steps, "n_dense": n_dense,
+            "gated_ms": ms, "gated_p10": percentile(sp, 10), "gated_p90": percentile(sp, 90),
+            "tokens_per_s": cfg.n_rows / (ms * 1e-3),
+            "dense_gated_ms": dms, "dense_gated_p10": percentile(dn, 10),
+            "dense_gated_p90": percentile(dn, 90), "speedup_over_dense": dms / ms}
+
+
 def dense_ffn(d):
     """The layer as a plain dense FFN through torch (hipBLASLt)."""
     b16 = d["b_up"].to(d["x"].dtype)
@@ -740,6 +784,8 @@ def main(argv=None):
                     help="skip the energy-per-token legs (amdsmi power telemetry)")
     ap.add_argument("--no-layers", action="store_true",
                     help="skip the other workloads timed beside the headline one")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the ReLU-gated layer against its dense torch form")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training step (sparse backward against dense autograd)")
     ap.add_argument("--no-conversions", action="store_true",
@@ -921,6 +967,12 @@ def main(argv=None):
             log(f"[bench] formats on {name}")
             result["formats"][name] = time_formats(CONFIGS[name], min(args.layer_steps, 10),
                                                    flush, dev)
+    if not args.no_gated:
+        result["gated"] = {}
+        for name in GATED_WORKLOADS:
+            log(f"[bench] gated layer {name}")
+            result["gated"][name] = time_gated(CONFIGS[name], min(args.layer_steps, 10),
+                                               min(args.warmup, 3), flush, dev)
     if not args.no_backward:
         result["backward"] = {}
         for name in BACKWARD_WORKLOADS:

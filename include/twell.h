@@ -185,6 +185,33 @@ int ffn_sparse_forward(const twell_shape* shape, const void* x, const void* w_up
                        const twell_hybrid* h_out, void* h_dense_debug, void* workspace,
                        size_t workspace_bytes, int32_t* d_status, void* stream);
 
+/* The ReLU-gated layer, y = (ReLU(x W_gate + b_gate) * (x W_up + b_up)) W_down,
+ * with its hidden activations h in hybrid TwELL form.  The pages describe
+ * only the non-gated layer ("The Relentless Search for Efficiency in
+ * Large-Scale Language Models", section "The Challenge of Sparsity Ignored by
+ * GPUs": the sparsity comes from the ReLU); this is the same method applied to
+ * the gated form of the sparse LLaMA models of "SakanaAI/sparser-faster-llms:
+ * How TwELL Makes Sparse Transformers Run Like They Were Built for Hopper",
+ * section "The Repo's Two Jobs".
+ *   1-2. steps 1-2 of ffn_sparse_forward on the gate (w_gate_t, b_gate): the
+ *        gate's activations ReLU(x W_gate + b_gate), rounded to the storage
+ *        type, are packed and routed; their non-zeros fix h's stored places;
+ *   2b.  at each stored place (row n, neuron j), the up branch
+ *        u = x[n] . w_up_t[j] + b_up[j] (float32) is taken and h = g * u,
+ *        rounded to the storage type, replaces the gate value g (u is computed
+ *        only where the gate is non-zero);
+ *   3-4. the hybrid down-projection of ffn_sparse_forward.
+ * A place whose u is 0 keeps a stored 0.  w_up_t [d_ff][d_model] dtype and
+ * b_up [d_ff] float32 as for the gate; the other arguments, the workspace
+ * (ffn_sparse_workspace_size), the status word and the errors are those of
+ * ffn_sparse_forward.  d_model up to 8192 (bf16) / 4096 (float32), else
+ * TWELL_ERR_UNSUPPORTED. */
+int ffn_sparse_gated_forward(const twell_shape* shape, const void* x, const void* w_gate_t,
+                             const float* b_gate, const void* w_up_t, const float* b_up,
+                             const void* w_down, void* y, const twell_hybrid* h_out,
+                             void* workspace, size_t workspace_bytes, int32_t* d_status,
+                             void* stream);
+
 /* ffn_sparse_forward that also records five caller-created HIP events
  * (stage_events[0..4], hipEvent_t passed as void*) on `stream`: before step
  * 1 and after each of steps 1-4.  Every stage here runs in its own launches
