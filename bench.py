@@ -47,23 +47,31 @@ STAGES = ("up_gemm_pack", "route", "spmm_sparse", "fallback_gemm")
 CALIB_COPY_BYTES = 256 << 20
 # kernels each stage launches for bf16 layers with d_model a multiple of 512
 STAGE_KERNELS = {
-    "up_gemm_pack": "up_pack_bf16_fast",
+    "up_gemm_pack": "up_pack_bf16_wave",
     "route": "row_or_kernel + materialize_kernel",
     "spmm_sparse": "spmm_list_bf16_kernel",
-    "fallback_gemm": "fallback_bf16_fast",
+    "fallback_gemm": "fallback_bf16_fast + fallback_reduce_kernel",
 }
 
 # sources of each stage's kernels: a recorded traffic figure stands only while they are unchanged
 _CSRC = "activation_sparse_transformer_amd/csrc/"
+_HDRS = (_CSRC + "common.h", _CSRC + "kernels.h", _CSRC + "spmm_split.h")
 STAGE_SOURCES = {
-    "up_gemm_pack": (_CSRC + "gemm_bf16.hip", _CSRC + "common.h", _CSRC + "kernels.h",
-                     _CSRC + "spmm_split.h"),
-    "route": (_CSRC + "route.hip", _CSRC + "common.h", _CSRC + "kernels.h",
-              _CSRC + "spmm_split.h"),
-    "spmm_sparse": (_CSRC + "spmm.hip", _CSRC + "common.h", _CSRC + "kernels.h",
-                    _CSRC + "spmm_split.h"),
-    "fallback_gemm": (_CSRC + "gemm_bf16.hip", _CSRC + "common.h", _CSRC + "kernels.h",
-                      _CSRC + "spmm_split.h"),
+    "up_gemm_pack": (_CSRC + "gemm_bf16.hip",) + _HDRS,
+    "route": (_CSRC + "route.hip",) + _HDRS,
+    "spmm_sparse": (_CSRC + "spmm.hip",) + _HDRS,
+    "fallback_gemm": (_CSRC + "gemm_bf16.hip",) + _HDRS,
+    # the 16-token decode layer's plain forward call
+    "decode_up": (_CSRC + "skinny.hip", _CSRC + "gemm_bf16.hip") + _HDRS,
+    "decode_route": (_CSRC + "route.hip",) + _HDRS,
+    "decode_down": (_CSRC + "gemm_bf16.hip", _CSRC + "skinny.hip") + _HDRS,
+    # the conversions
+    "twell_pack": (_CSRC + "route.hip",) + _HDRS,
+    "twell_unpack": (_CSRC + "route.hip",) + _HDRS,
+    # the backward (its dx runs the hybrid product's kernels) and the gated up branch
+    "backward": (_CSRC + "backward.hip", _CSRC + "vec_ops.h", _CSRC + "spmm.hip",
+                 _CSRC + "gemm_bf16.hip") + _HDRS,
+    "gated_up": (_CSRC + "gate.hip", _CSRC + "vec_ops.h") + _HDRS,
 }
 
 
@@ -193,6 +201,9 @@ def time_layer(cfg, steps, warmup, flush, dev, t=None):
            "dense_ffn_ms": dms, "dense_ffn_p10": percentile(dense, 10),
            "dense_ffn_p90": percentile(dense, 90),
            "speedup_twell_over_dense": dms / ms}
+    tr = recorded_traffic(cfg.name, ("decode_up", "decode_route", "decode_down"))
+    if all(v is not None for v in tr.values()):
+        out["traffic_per_forward"] = sum(tr.values())
     del d
     torch.cuda.empty_cache()
     return out
@@ -205,7 +216,7 @@ def time_layer(cfg, steps, warmup, flush, dev, t=None):
 # then run on the headline layer only, so their per-kernel profile averages
 # are the headline's.
 CONVERSION_WORKLOAD = "large_bf16"
-PACK_KERNELS = "pack_tiles_kernel + row_or_kernel + route_scan_kernel + materialize_kernel"
+PACK_KERNELS = "pack_tiles_kernel + row_or_kernel + materialize_kernel"
 UNPACK_KERNELS = "unpack_kernel"
 
 
@@ -265,19 +276,21 @@ def time_conversions(cfg, steps, warmup, flush, dev, t=None):
     nnz = int(torch.count_nonzero(h).item())
     nbytes = conversion_bytes(cfg.n_rows, cfg.d_ff, cfg.tile, cfg.capacity, e, n_dense)
 
-    def stage(ms_list, kernels):
+    traffic = recorded_traffic(f"{cfg.name}_conversions", ("twell_pack", "twell_unpack"))
+
+    def stage(name, ms_list, kernels):
         ms = median(ms_list)
         gbs = nbytes / (ms * 1e-3) / 1e9
         return {"ms": ms, "ms_p10": percentile(ms_list, 10), "ms_p90": percentile(ms_list, 90),
                 "bound": "hbm", "bytes_per_launch": nbytes, "achieved": gbs, "unit": "GB/s",
-                "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                "peak": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS, "traffic": traffic[name],
                 "kernels": kernels}
 
     out = {"workload": cfg.name, "n_rows": cfg.n_rows, "d_ff": cfg.d_ff, "tile": cfg.tile,
            "capacity": cfg.capacity, "h": "ReLU(x W_up^T + b) of the layer's inputs, torch bf16",
            "active_fraction": nnz / (cfg.n_rows * cfg.d_ff), "n_dense": n_dense,
-           "twell_pack": stage(pack_ms, PACK_KERNELS),
-           "twell_unpack": stage(unpack_ms, UNPACK_KERNELS),
+           "twell_pack": stage("twell_pack", pack_ms, PACK_KERNELS),
+           "twell_unpack": stage("twell_unpack", unpack_ms, UNPACK_KERNELS),
            "roundtrip_bitwise_equal": True}
     del h, hy, ws, back
     torch.cuda.empty_cache()
@@ -579,6 +592,9 @@ def time_backward(cfg, steps, warmup, flush, dev, t=None):
     ms, dms, st, dst = median(sb), median(db_ms), median(sstep), median(dstep)
     e = cfg.elem_bytes
     N, dm, dff = cfg.n_rows, cfg.d_model, cfg.d_ff
+    # compulsory HBM bytes of one call: x, dy, both weights and the stored h
+    # read; dx, the float32 weight gradients and db written
+    bwd_bytes = 3 * N * dm * e + 2 * dff * dm * e + stored + 2 * dff * dm * 4 + dff * 4
     return {
         "workload": cfg.name, "n_rows": N, "d_model": dm, "d_ff": dff, "tile": cfg.tile,
         "capacity": cfg.capacity, "steps": steps, "n_dense": n_dense, "nonzeros_h": nnz,
@@ -597,6 +613,11 @@ def time_backward(cfg, steps, warmup, flush, dev, t=None):
         "stored_activation_bytes_dense": N * dff * e,
         "sparse_backward_workspace_bytes": ws_bytes,
         "weight_grad_dtype": {"sparse": "f32", "dense": cfg.dtype},
+        "hbm_roofline": {"bound": "hbm", "bytes_per_call": bwd_bytes,
+                         "achieved": bwd_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                         "peak": HBM_PEAK_GBS,
+                         "frac": bwd_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic(f"{cfg.name}_backward", ("backward",))["backward"]},
     }
 
 
@@ -641,7 +662,8 @@ def time_gated(cfg, steps, warmup, flush, dev):
             "gated_ms": ms, "gated_p10": percentile(sp, 10), "gated_p90": percentile(sp, 90),
             "tokens_per_s": cfg.n_rows / (ms * 1e-3),
             "dense_gated_ms": dms, "dense_gated_p10": percentile(dn, 10),
-            "dense_gated_p90": percentile(dn, 90), "speedup_over_dense": dms / ms}
+            "dense_gated_p90": percentile(dn, 90), "speedup_over_dense": dms / ms,
+            "traffic_up_branch": recorded_traffic(f"{cfg.name}_gated", ("gated_up",))["gated_up"]}
 
 
 def dense_ffn(d):
@@ -664,15 +686,16 @@ def source_sha(stage: str) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str) -> dict:
-    """HBM bytes per launch of each stage from the committed hardware-counter summary.
+def recorded_traffic(summary: str, stages=STAGES) -> dict:
+    """HBM bytes per launch of each stage from a committed hardware-counter summary
+    (profiles/<summary>_hbm_traffic.txt).
 
     The summary holds FETCH_SIZE / WRITE_SIZE per kernel already scaled to bytes
-    by a plain copy of known size; a stage whose sources changed since the
-    counters were taken gets None.
+    by a plain copy of known size; a stage's figure is the sum over its kernels,
+    and a stage whose sources changed since the counters were taken gets None.
     """
-    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
-    out = {s: None for s in STAGES}
+    path = os.path.join(ROOT, "profiles", f"{summary}_hbm_traffic.txt")
+    out = {s: None for s in stages}
     if not os.path.exists(path):
         return out
     per = {}
@@ -683,6 +706,8 @@ def recorded_traffic(workload: str) -> dict:
                 continue
             kv = dict(zip(f[0::2], f[1::2]))
             stage = kv["stage"]
+            if stage not in out:
+                continue
             ok = kv["src_sha"] == source_sha(stage)
             prev = per.get(stage, 0.0)
             per[stage] = None if (prev is None or not ok) else prev + float(kv["bytes"])
