@@ -1079,15 +1079,264 @@ __device__ __forceinline__ void up_pack_epilogue_wave(
   }
 }
 
-// Fast G1 with waves of 64 x 128: each wave owns whole tiles of T = 64 or 128
-// for its rows, so the pack needs no exchange between waves.
-template <class CF, int T, bool HDEBUG>
+// The lowest remaining element of a segment given as its even (bit m: element
+// 2 m) and odd (bit m: element 2 m + 1) non-zero masks, which loses that bit.
+// Returns 0xfffffffe or more when both masks are empty.
+__device__ __forceinline__ uint32_t ffbl64(uint64_t m) {
+  // find-first-bit gives 0xffffffff for 0; OR-ing 32 keeps that and adds 32 otherwise
+  uint32_t lo, hi;
+  asm("v_ffbl_b32 %0, %1" : "=v"(lo) : "v"(static_cast<uint32_t>(m)));
+  asm("v_ffbl_b32 %0, %1" : "=v"(hi) : "v"(static_cast<uint32_t>(m >> 32)));
+  return min(lo, hi | 32u);
+}
+
+__device__ __forceinline__ uint32_t lowest_element(uint64_t& ev, uint64_t& od) {
+  const uint32_t e0 = 2u * ffbl64(ev), e1 = 2u * ffbl64(od) + 1u;
+  const bool even = e0 < e1;
+  if (even) ev &= ev - 1; else od &= od - 1;
+  return even ? e0 : e1;
+}
+
+// dst[0, bytes) = src[0, bytes) in the widest unit that divides both
+// addresses and the length (src in LDS).
+__device__ __forceinline__ void copy_run(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+                                         int bytes) {
+  const uint32_t al = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)) |
+                      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(src)) |
+                      static_cast<uint32_t>(bytes);
+  if ((al & 15u) == 0) {
+    for (int o = 0; o < bytes; o += 16)
+      *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(src + o);
+  } else if ((al & 7u) == 0) {
+    for (int o = 0; o < bytes; o += 8)
+      *reinterpret_cast<uint2*>(dst + o) = *reinterpret_cast<const uint2*>(src + o);
+  } else if ((al & 3u) == 0) {
+    for (int o = 0; o < bytes; o += 4)
+      *reinterpret_cast<uint32_t*>(dst + o) = *reinterpret_cast<const uint32_t*>(src + o);
+  } else if ((al & 1u) == 0) {
+    for (int o = 0; o < bytes; o += 2)
+      *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(src + o);
+  } else {
+    for (int o = 0; o < bytes; ++o) dst[o] = src[o];
+  }
+}
+
+// ReLU of an accumulator: v_max_f32 against 0 gives 0 for a negative, -0 or
+// NaN z (MFMA results are never signalling NaNs), as z > 0 ? z : 0 does.
+__device__ __forceinline__ float relu_acc(float z) {
+  float o;
+  asm("v_max_f32 %0, 0, %1" : "=v"(o) : "v"(z));
+  return o;
+}
+
+// 16-byte chunk swizzle of the LDS h tile: rows 4 q .. 4 q + 3 share
+// bitrev4(q & 15), so a lane's 4 rows of one MFMA register group sit at fixed
+// offsets, the two row halves of a write (rows 4 apart) land 8 chunks apart,
+// and 16 rows 4 apart read by 16 lanes hit 16 distinct chunk columns.
+__device__ __forceinline__ int hswz(int row) {
+  const int q = (row >> 2) & 15;
+  return ((q & 1) << 3) | ((q & 2) << 1) | ((q & 4) >> 1) | ((q & 8) >> 3);
+}
+
+// Pack epilogue through LDS for 256-column blocks.  The block's h (ReLU, then
+// bf16) goes to LDS as a [BM][256] tile of 512-byte rows with hswz-swizzled
+// 16-byte chunks.  Then each thread packs whole (row, tile) segments (per
+// wave 64 rows of one tile, rows 4 apart in each 16-lane group): a non-zero
+// mask over the segment (two elements per 32-bit word test), its count, and
+// the first non-zeros in ascending column order, stored straight to the TwELL
+// arrays; an overflowing segment gets count 0, flag 1, padding slots, and its
+// raw h in the spill area.  CMAX bounds C (slots are unrolled CMAX times,
+// those past C predicated off).
+template <class CF, int T, int CMAX, bool HDEBUG>
+__device__ __forceinline__ void up_pack_epilogue_lds(
+    const fast::f32x16_t (&acc)[CF::WTM / 32][CF::WTN / 32], uint8_t* __restrict__ lds,
+    int m0, int n0, int M, int N, int C, int nt,
+    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
+  constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32, BM = CF::BM, BN = CF::BN;
+  static_assert(BN == 256 && CF::WTM == 64 && CF::WTN == 128, "512-byte LDS rows, 64 x 128 waves");
+  static_assert(T == 64 || T == 128, "whole 16-byte chunks, at most 4 mask words per segment");
+  static_assert(CMAX % 4 == 0, "whole words of slots");
+  constexpr int ROWB = BN * 2;   // bytes per LDS row
+  constexpr int CH = T / 8;      // 16-byte chunks per segment
+  constexpr int MW = T / 32;     // mask words per segment
+  constexpr int TPB = BN / T;    // segments per row of the block
+  // C <= 8: the slots are staged in LDS after the h tile and stored by rows
+  constexpr bool STAGED = CMAX <= 8;
+  static_assert(!STAGED || CF::NT == 2 * BM, "two threads per row for the stores");
+  uint16_t* sv = reinterpret_cast<uint16_t*>(lds + BM * ROWB);  // [BM][TPB * C]
+  uint8_t* si = reinterpret_cast<uint8_t*>(sv + BM * TPB * C);  // [BM][TPB * C]
+  uint8_t* sc = si + BM * TPB * C;                               // [BM][TPB]
+  uint8_t* sf = sc + BM * TPB;                                   // [BM][TPB]
+  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
+  const int hh = lane >> 5, c = lane & 31;
+  {
+    // register 4 p + s of block (i, j) is row wm 64 + i 32 + p 8 + 4 hh + s,
+    // column wn 128 + j 32 + c; its chunk is (wn 16 + j 4 + c / 8) ^ hswz(row)
+    // = lanepart ^ cp(i, j, p), with hswz(row) = 8 hh ^ cp-bits of (i, p)
+    const uint32_t lanepart = static_cast<uint32_t>(wn * 16 + ((c >> 3) ^ (hh << 3))) << 4;
+    uint8_t* lb = lds + (wm * 64 + 4 * hh) * ROWB + (c & 7) * 2;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t cp = static_cast<uint32_t>(((j ^ (p & 1)) << 2) ^ ((p >> 1) << 1) ^ i) << 4;
+          uint8_t* a = lb + (lanepart ^ cp) + (i * 32 + p * 8) * ROWB;
+#pragma unroll
+          for (int s = 0; s < 4; s += 2) {
+            const f32x2_t z = {relu_acc(acc[i][j][4 * p + s]), relu_acc(acc[i][j][4 * p + s + 1])};
+            const uint32_t hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2_t));
+            *reinterpret_cast<uint16_t*>(a + s * ROWB) = static_cast<uint16_t>(hp);
+            *reinterpret_cast<uint16_t*>(a + (s + 1) * ROWB) = static_cast<uint16_t>(hp >> 16);
+          }
+        }
+  }
+  __syncthreads();
+  const int t0 = n0 / T;
+  for (int it = threadIdx.x; it < BM * TPB; it += CF::NT) {
+    const int tl = it / BM, within = it % BM;
+    const int r = (within & ~63) + 4 * (within & 15) + ((within >> 4) & 3);
+    const int n = m0 + r, t = t0 + tl;
+    if (n >= M || t >= nt) continue;
+    const uint8_t* rowp = lds + r * ROWB;
+    const int sw = hswz(r);
+    uint32_t mask[MW];
+#pragma unroll
+    for (int w = 0; w < MW; ++w) mask[w] = 0u;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const uint4 d = *reinterpret_cast<const uint4*>(rowp + (((tl * CH + k) ^ sw) << 4));
+      if constexpr (HDEBUG)
+        *reinterpret_cast<uint4*>(hdebug + static_cast<int64_t>(n) * N + t * T + k * 8) = d;
+      const uint32_t dd[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // bit 0 / 16 set when the low / high bf16 is non-zero (sign ignored)
+        uint32_t f;
+        asm("v_pk_min_u16 %0, %1, %2" : "=v"(f) : "v"(dd[q] & 0x7fff7fffu), "s"(0x00010001u));
+        mask[k / 4] |= f << ((k % 4) * 4 + q);
+      }
+    }
+    int count = 0;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) count += __popc(mask[w]);
+    const bool fits = count <= C;
+    // even / odd elements of the segment: bit m of ev / od is element 2 m / 2 m + 1
+    uint64_t ev = 0, od = 0;
+#pragma unroll
+    for (int w = 0; w < MW; ++w) {
+      ev |= static_cast<uint64_t>(mask[w] & 0xffffu) << (16 * w);
+      od |= static_cast<uint64_t>(mask[w] >> 16) << (16 * w);
+    }
+    if (!fits) ev = od = 0;
+    uint32_t vp[CMAX / 2], ip[CMAX / 4];
+#pragma unroll
+    for (int k = 0; k < CMAX / 2; ++k) vp[k] = 0u;
+#pragma unroll
+    for (int k = 0; k < CMAX / 4; ++k) ip[k] = 0u;
+#pragma unroll
+    for (int k = 0; k < CMAX; ++k) {
+      if (k >= C) break;
+      const uint32_t e = lowest_element(ev, od);  // >= 2^31 when none is left
+      if (e < 0x80000000u) {
+        const int lc = tl * T + static_cast<int>(e);  // column inside the block
+        const uint32_t v = *reinterpret_cast<const uint16_t*>(
+            rowp + (((lc >> 3) ^ sw) << 4) + ((lc & 7) << 1));
+        vp[k / 2] |= v << (16 * (k % 2));
+        ip[k / 4] |= e << (8 * (k % 4));
+      }
+    }
+    if (!fits && spill != nullptr) {
+#pragma unroll
+      for (int k = 0; k < CH; ++k)
+        *reinterpret_cast<uint4*>(spill + static_cast<int64_t>(n) * N + t * T + k * 8) =
+            *reinterpret_cast<const uint4*>(rowp + (((tl * CH + k) ^ sw) << 4));
+    }
+    if constexpr (STAGED) {
+      // the row's run of TPB * C slots in LDS, stored by rows below
+      const int o = r * TPB * C + tl * C;
+      if ((C & 1) == 0) {
+#pragma unroll
+        for (int k = 0; k < CMAX / 2; ++k)
+          if (2 * k < C) reinterpret_cast<uint32_t*>(sv + o)[k] = vp[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < CMAX; ++k)
+          if (k < C) sv[o + k] = static_cast<uint16_t>(vp[k / 2] >> (16 * (k % 2)));
+      }
+      if ((C & 3) == 0) {
+#pragma unroll
+        for (int k = 0; k < CMAX / 4; ++k)
+          if (4 * k < C) reinterpret_cast<uint32_t*>(si + o)[k] = ip[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < CMAX; ++k)
+          if (k < C) si[o + k] = static_cast<uint8_t>(ip[k / 4] >> (8 * (k % 4)));
+      }
+      sc[r * TPB + tl] = static_cast<uint8_t>(fits ? count : 0);
+      sf[r * TPB + tl] = fits ? 0 : 1;
+    } else {
+      const int64_t g = (static_cast<int64_t>(n) * nt + t) * C;
+      if ((C & 1) == 0) {
+#pragma unroll
+        for (int k = 0; k < CMAX / 2; ++k)
+          if (2 * k < C) reinterpret_cast<uint32_t*>(vals + g)[k] = vp[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < CMAX; ++k)
+          if (k < C) vals[g + k] = static_cast<uint16_t>(vp[k / 2] >> (16 * (k % 2)));
+      }
+      if ((C & 3) == 0) {
+#pragma unroll
+        for (int k = 0; k < CMAX / 4; ++k)
+          if (4 * k < C) reinterpret_cast<uint32_t*>(idx + g)[k] = ip[k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < CMAX; ++k)
+          if (k < C) idx[g + k] = static_cast<uint8_t>(ip[k / 4] >> (8 * (k % 4)));
+      }
+      cnt[static_cast<int64_t>(n) * nt + t] = static_cast<uint8_t>(fits ? count : 0);
+      flags[static_cast<int64_t>(n) * nt + t] = fits ? 0 : 1;
+    }
+  }
+  if constexpr (STAGED) {
+    // one thread per row and array group: a row's runs are contiguous in every array
+    __syncthreads();
+    const int r = threadIdx.x % BM;
+    const int n = m0 + r;
+    const int tv = min(TPB, nt - t0);  // tiles of the block inside d_ff
+    if (n < M && tv > 0) {
+      const int64_t g = static_cast<int64_t>(n) * nt + t0;
+      if (threadIdx.x < BM) {
+        copy_run(reinterpret_cast<uint8_t*>(vals + g * C),
+                 reinterpret_cast<const uint8_t*>(sv + r * TPB * C), tv * C * 2);
+      } else {
+        copy_run(idx + g * C, si + r * TPB * C, tv * C);
+        copy_run(cnt + g, sc + r * TPB, tv);
+        copy_run(flags + g, sf + r * TPB, tv);
+      }
+    }
+  }
+}
+
+// Fast G1 with waves of 64 x 128 on 256-column blocks, packed through LDS
+// (C <= CMAX).
+template <class CF, int T, int CMAX, bool HDEBUG>
 __global__ __launch_bounds__(CF::NT) void up_pack_bf16_wave(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_up_t,
     const float* __restrict__ bias, int M, int N, int K, int C, int nt,
     uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
     uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE];
+  // two operand stages, which the epilogue reuses for the h tile; then, for
+  // C <= 8, the staged slots: (2 + 1) bytes per slot and 2 per (row, tile)
+  constexpr int STAGED_BYTES = CMAX <= 8 ? CF::BM * (CF::BN / T) * (3 * CMAX + 2) : 0;
+  static_assert(2 * CF::STAGE * 2 >= CF::BM * CF::BN * 2, "the h tile fits the stages");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * CF::STAGE + STAGED_BYTES / 2];
   int m0, n0;
   fast::tile_coords<4>((M + CF::BM - 1) / CF::BM, (N + CF::BN - 1) / CF::BN, CF::BM, CF::BN, m0, n0);
   fast::f32x16_t acc[CF::WTM / 32][CF::WTN / 32];
@@ -1101,8 +1350,8 @@ __global__ __launch_bounds__(CF::NT) void up_pack_bf16_wave(
     }
   }
   fast::mainloop32_pipe<CF>(x, K, M, m0, w_up_t, K, N, n0, K, lds, bj, acc);
-  up_pack_epilogue_wave<CF, T, HDEBUG>(acc, reinterpret_cast<uint8_t*>(lds), m0, n0, M, N, C, nt,
-                                       vals, idx, cnt, flags, spill, hdebug);
+  up_pack_epilogue_lds<CF, T, CMAX, HDEBUG>(acc, reinterpret_cast<uint8_t*>(lds), m0, n0, M, N, C,
+                                            nt, vals, idx, cnt, flags, spill, hdebug);
 }
 
 // ---------------------------------------------------------------- G4 kernel
@@ -1445,9 +1694,15 @@ hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint1
     const int blocks =
         ((M + BigCfgW::BM - 1) / BigCfgW::BM) * ((N + BigCfgW::BN - 1) / BigCfgW::BN);
     auto go = [&](auto t, auto dbg) {
-      up_pack_bf16_wave<BigCfgW, decltype(t)::value, decltype(dbg)::value>
-          <<<blocks, BigCfgW::NT, 0, s>>>(x, w_up_t, b_up, M, N, K, g.capacity, g.n_tiles, vals,
-                                         out.idx, out.cnt, out.flags, spill, hdbg);
+      constexpr int T = decltype(t)::value, CBIG = kStagedSlots / (BigCfgW::BN / T);
+      if (g.capacity <= 8)
+        up_pack_bf16_wave<BigCfgW, T, 8, decltype(dbg)::value>
+            <<<blocks, BigCfgW::NT, 0, s>>>(x, w_up_t, b_up, M, N, K, g.capacity, g.n_tiles,
+                                           vals, out.idx, out.cnt, out.flags, spill, hdbg);
+      else
+        up_pack_bf16_wave<BigCfgW, T, CBIG, decltype(dbg)::value>
+            <<<blocks, BigCfgW::NT, 0, s>>>(x, w_up_t, b_up, M, N, K, g.capacity, g.n_tiles,
+                                           vals, out.idx, out.cnt, out.flags, spill, hdbg);
     };
     using I64 = std::integral_constant<int, 64>;
     using I128 = std::integral_constant<int, 128>;
