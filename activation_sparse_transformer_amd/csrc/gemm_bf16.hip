@@ -909,176 +909,6 @@ __global__ __launch_bounds__(CF::NT) void up_pack_bf16_fast(
                                   nt, vals, idx, cnt, flags, spill, hdebug);
 }
 
-// Epilogue for waves that own whole TwELL tiles (wave tile 64 rows x 128
-// columns, T = 64 or 128, block slots staged in LDS).  In the 32x32 MFMA
-// output layout register r of block (i, j) holds, in lanes 0-31, row
-// i*32 + (r/4)*8 + r%4 and in lanes 32-63 the row 4 below, at column
-// j*32 + lane%32; one ballot per (i, r, j) is the non-zero pattern of 32
-// columns of those two rows.  A row's tile lies in this wave's own ballots,
-// so its count, overflow and every slot position are wave-local (scalar sums
-// of ballot halves plus a lane's position among the set bits below it): no
-// counts cross waves and no barrier sits between the ballots and the stores.
-// Blocks of 32 columns without a non-zero in either row are skipped by a
-// scalar branch; inside, every lane stores, lanes without a slot to write into
-// a word of their own past the staged slots (no exec-mask branches).
-template <int L>
-__device__ __forceinline__ int set_lane(int v, int val) {
-  asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(val), "i"(L));
-  return v;
-}
-
-// lane `sel` (0..63, a constant once the callers' loops are unrolled) of v = val
-__device__ __forceinline__ int set_lane_dyn(int v, int val, int sel) {
-#define TW_SET(L) if (sel == L) return set_lane<L>(v, val);
-#define TW_SET8(B) TW_SET(B) TW_SET(B + 1) TW_SET(B + 2) TW_SET(B + 3) TW_SET(B + 4) TW_SET(B + 5) TW_SET(B + 6) TW_SET(B + 7)
-  TW_SET8(0) TW_SET8(8) TW_SET8(16) TW_SET8(24) TW_SET8(32) TW_SET8(40) TW_SET8(48) TW_SET8(56)
-#undef TW_SET8
-#undef TW_SET
-  return v;
-}
-
-template <class CF, int T, bool HDEBUG>
-__device__ __forceinline__ void up_pack_epilogue_wave(
-    const fast::f32x16_t (&acc)[CF::WTM / 32][CF::WTN / 32], uint8_t* __restrict__ lds,
-    int m0, int n0, int M, int N, int C, int nt,
-    uint16_t* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
-    uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
-  constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32, BM = CF::BM;
-  static_assert(CF::WTN == 128 && FN == 4, "a wave owns 128 columns");
-  static_assert(T == 64 || T == 128, "whole tiles per wave");
-  constexpr int TPW = 128 / T;  // tiles per wave
-  constexpr int JPT = T / 32;   // 32-column blocks per tile
-  typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
-  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-  uint16_t* sv = reinterpret_cast<uint16_t*>(lds);        // [BM][kStagedSlots] (+ 64 dummies)
-  uint8_t* si = lds + (BM * kStagedSlots + kWave) * 2;     // [BM][kStagedSlots] (+ 64 dummies)
-  uint8_t* sc = si + BM * kStagedSlots + kWave;            // [BM][4]
-  uint8_t* sf = sc + BM * 4;                               // [BM][4]
-  for (int e = threadIdx.x; e < BM * kStagedSlots / 2; e += CF::NT) {
-    reinterpret_cast<uint32_t*>(sv)[e] = 0u;
-    if (e < BM * kStagedSlots / 4) reinterpret_cast<uint32_t*>(si)[e] = 0u;
-  }
-  __syncthreads();
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
-  const int hh = lane >> 5, c = lane & 31;
-  const int colw = n0 + wn * 128;       // first column of the wave, tile-aligned
-  const int tbw = (wn * 128) / T;        // the wave's first tile inside the block
-  const int rw0 = wm * CF::WTM;          // the wave's first row inside the block
-  const int dummy = BM * kStagedSlots + lane;  // this lane's slot for stores that do not count
-  const int row_lim = M - (m0 + rw0);    // rows of the wave below this are inside h
-  const bool wave_cols = colw < N;       // whole tiles: all 128 columns in or out (T | d_ff)
-  int cv[TPW];  // lane q: count of row q's tile (256 = overflow)
-#pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) cv[tt] = 0;
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    uint32_t hp[FN][8];
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float z0 = acc[i][j][r], z1 = acc[i][j][r + 1];  // the bias is already in
-        const f32x2_t z = {z0 > 0.f ? z0 : 0.f, z1 > 0.f ? z1 : 0.f};
-        hp[j][r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(z, bf16x2_t));
-      }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qa = i * 32 + (r >> 2) * 8 + (r & 3);  // row of lanes 0-31 inside the wave
-      const int q = qa + hh * 4;                       // this lane's row inside the wave
-      const bool row_ok = q < row_lim && wave_cols;
-      uint32_t v[FN];
-      uint64_t b[FN];
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        v[j] = (r & 1) ? (hp[j][r / 2] >> 16) : (hp[j][r / 2] & 0xffffu);
-        b[j] = wave_ballot(v[j] != 0u);
-      }
-      if constexpr (HDEBUG) {
-        if (row_ok)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            hdebug[static_cast<int64_t>(m0 + rw0 + q) * N + colw + j * 32 + c] =
-                static_cast<uint16_t>(v[j]);
-      }
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        int la[JPT], ca = 0, cb = 0;
-#pragma unroll
-        for (int jj = 0; jj < JPT; ++jj) {
-          const uint64_t m = b[tt * JPT + jj];
-          la[jj] = __popc(static_cast<uint32_t>(m));
-          ca += la[jj];
-          cb += __popc(static_cast<uint32_t>(m >> 32));
-        }
-        const bool fa = ca <= C, fb = cb <= C;
-        cv[tt] = set_lane_dyn(cv[tt], fa ? ca : 256, qa);
-        cv[tt] = set_lane_dyn(cv[tt], fb ? cb : 256, qa + 4);
-        const bool fits = hh ? fb : fa;
-        int before_a = 0, before_b = 0;
-#pragma unroll
-        for (int jj = 0; jj < JPT; ++jj) {
-          const int j = tt * JPT + jj;
-          const uint64_t m = b[j];
-          const int lb = __popc(static_cast<uint32_t>(m >> 32));
-          if (m != 0 && (fa || fb)) {  // scalar branch: a non-zero to place
-            // mbcnt_lo adds all of the low half's bits for lanes 32-63: seed
-            // those with before_b - la, lanes 0-31 with before_a
-            const int seed = hh ? before_b - la[jj] : before_a;
-            const int pos = static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                static_cast<uint32_t>(m >> 32),
-                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), static_cast<uint32_t>(seed))));
-            const bool st = v[j] != 0u && fits && row_ok;
-            const int sl = st ? (rw0 + q) * kStagedSlots + (tbw + tt) * C + pos : dummy;
-            sv[sl] = static_cast<uint16_t>(v[j]);
-            si[sl] = static_cast<uint8_t>(jj * 32 + c);
-          }
-          before_a += la[jj];
-          before_b += lb;
-        }
-        if (spill != nullptr && !(fa && fb)) {  // scalar branch: a row of the pair overflowed
-#pragma unroll
-          for (int jj = 0; jj < JPT; ++jj)
-            if (!fits && row_ok)
-              spill[static_cast<int64_t>(m0 + rw0 + q) * N + colw + (tt * JPT + jj) * 32 + c] =
-                  static_cast<uint16_t>(v[tt * JPT + jj]);
-        }
-      }
-    }
-  }
-  // counts and flags of the wave's rows: lane q holds row q's
-  if (lane < CF::WTM) {
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      sc[(rw0 + lane) * 4 + tbw + tt] = static_cast<uint8_t>(cv[tt] & 0xff);
-      sf[(rw0 + lane) * 4 + tbw + tt] = static_cast<uint8_t>(cv[tt] >> 8);
-    }
-  }
-  __syncthreads();
-  // copy the block's slots out: each row owns one contiguous run per array
-  const int tpb = CF::BN / T;
-  const int t0 = n0 / T;
-  const int tv = min(tpb, nt - t0);  // tiles of the block inside d_ff
-  const int run = tv * C;
-  for (int e = threadIdx.x; e < BM * run; e += CF::NT) {
-    const int rl = e / run, k = e - (e / run) * run;
-    const int n = m0 + rl;
-    if (n < M) {
-      const int64_t g = (static_cast<int64_t>(n) * nt + t0) * C + k;
-      vals[g] = sv[rl * kStagedSlots + k];
-      idx[g] = si[rl * kStagedSlots + k];
-    }
-  }
-  for (int e = threadIdx.x; e < BM * tv; e += CF::NT) {
-    const int rl = e / tv, k = e - (e / tv) * tv;
-    const int n = m0 + rl;
-    if (n < M) {
-      cnt[static_cast<int64_t>(n) * nt + t0 + k] = sc[rl * 4 + k];
-      flags[static_cast<int64_t>(n) * nt + t0 + k] = sf[rl * 4 + k];
-    }
-  }
-}
-
 // The lowest remaining element of a segment given as its even (bit m: element
 // 2 m) and odd (bit m: element 2 m + 1) non-zero masks, which loses that bit.
 // Returns 0xfffffffe or more when both masks are empty.
