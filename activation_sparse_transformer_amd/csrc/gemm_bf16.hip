@@ -920,11 +920,29 @@ __device__ __forceinline__ uint32_t ffbl64(uint64_t m) {
   return min(lo, hi | 32u);
 }
 
-__device__ __forceinline__ uint32_t lowest_element(uint64_t& ev, uint64_t& od) {
-  const uint32_t e0 = 2u * ffbl64(ev), e1 = 2u * ffbl64(od) + 1u;
-  const bool even = e0 < e1;
-  if (even) ev &= ev - 1; else od &= od - 1;
-  return even ? e0 : e1;
+// Word w of ev / od covers elements [128 w, 128 w + 128).
+template <int EW>
+__device__ __forceinline__ uint32_t lowest_element(uint64_t (&ev)[EW], uint64_t (&od)[EW]) {
+  uint32_t e = 0xffffffffu;
+  int hit = -1;
+  bool even = false;
+#pragma unroll
+  for (int w = 0; w < EW; ++w) {
+    const uint32_t e0 = 2u * ffbl64(ev[w]), e1 = 2u * ffbl64(od[w]) + 1u;
+    const uint32_t ew = min(e0, e1);
+    if (hit < 0 && ew < 0x80000000u) {
+      hit = w;
+      even = e0 < e1;
+      e = ew + 128u * w;
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < EW; ++w) {
+    if (w == hit) {
+      if (even) ev[w] &= ev[w] - 1; else od[w] &= od[w] - 1;
+    }
+  }
+  return e;
 }
 
 // dst[0, bytes) = src[0, bytes) in the widest unit that divides both
@@ -985,7 +1003,7 @@ __device__ __forceinline__ void up_pack_epilogue_lds(
     uint8_t* __restrict__ flags, uint16_t* __restrict__ spill, uint16_t* __restrict__ hdebug) {
   constexpr int FM = CF::WTM / 32, FN = CF::WTN / 32, BM = CF::BM, BN = CF::BN;
   static_assert(BN == 256 && CF::WTM == 64 && CF::WTN == 128, "512-byte LDS rows, 64 x 128 waves");
-  static_assert(T == 64 || T == 128, "whole 16-byte chunks, at most 4 mask words per segment");
+  static_assert(T == 64 || T == 128 || T == 256, "whole 16-byte chunks, whole tiles per block");
   static_assert(CMAX % 4 == 0, "whole words of slots");
   constexpr int ROWB = BN * 2;   // bytes per LDS row
   constexpr int CH = T / 8;      // 16-byte chunks per segment
@@ -1056,14 +1074,21 @@ __device__ __forceinline__ void up_pack_epilogue_lds(
 #pragma unroll
     for (int w = 0; w < MW; ++w) count += __popc(mask[w]);
     const bool fits = count <= C;
-    // even / odd elements of the segment: bit m of ev / od is element 2 m / 2 m + 1
-    uint64_t ev = 0, od = 0;
+    // even / odd elements of the segment: bit m of ev / od (over its 64-bit
+    // words) is element 2 m / 2 m + 1
+    constexpr int EW = (T + 127) / 128;
+    uint64_t ev[EW], od[EW];
+#pragma unroll
+    for (int w = 0; w < EW; ++w) ev[w] = od[w] = 0;
 #pragma unroll
     for (int w = 0; w < MW; ++w) {
-      ev |= static_cast<uint64_t>(mask[w] & 0xffffu) << (16 * w);
-      od |= static_cast<uint64_t>(mask[w] >> 16) << (16 * w);
+      ev[w / 4] |= static_cast<uint64_t>(mask[w] & 0xffffu) << (16 * (w % 4));
+      od[w / 4] |= static_cast<uint64_t>(mask[w] >> 16) << (16 * (w % 4));
     }
-    if (!fits) ev = od = 0;
+    if (!fits) {
+#pragma unroll
+      for (int w = 0; w < EW; ++w) ev[w] = od[w] = 0;
+    }
     uint32_t vp[CMAX / 2], ip[CMAX / 4];
 #pragma unroll
     for (int k = 0; k < CMAX / 2; ++k) vp[k] = 0u;
@@ -1072,7 +1097,7 @@ __device__ __forceinline__ void up_pack_epilogue_lds(
 #pragma unroll
     for (int k = 0; k < CMAX; ++k) {
       if (k >= C) break;
-      const uint32_t e = lowest_element(ev, od);  // >= 2^31 when none is left
+      const uint32_t e = lowest_element<EW>(ev, od);  // >= 2^31 when none is left
       if (e < 0x80000000u) {
         const int lc = tl * T + static_cast<int>(e);  // column inside the block
         const uint32_t v = *reinterpret_cast<const uint16_t*>(
@@ -1519,12 +1544,16 @@ hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint1
   auto* vals = static_cast<uint16_t*>(out.vals);
   auto* spill = static_cast<uint16_t*>(out.spill);
   auto* hdbg = static_cast<uint16_t*>(out.h_debug);
-  if (M >= 128 && K % 64 == 0 && (g.tile == 64 || g.tile == 128) && N % 128 == 0 &&
+  const bool wave_tile = g.tile == 64 || g.tile == 128 || (g.tile == 256 && g.capacity <= 8);
+  if (M >= 128 && K % 64 == 0 && wave_tile && N % g.tile == 0 &&
       (BigCfgW::BN / g.tile) * g.capacity <= kStagedSlots) {
     const int blocks =
         ((M + BigCfgW::BM - 1) / BigCfgW::BM) * ((N + BigCfgW::BN - 1) / BigCfgW::BN);
     auto go = [&](auto t, auto dbg) {
-      constexpr int T = decltype(t)::value, CBIG = kStagedSlots / (BigCfgW::BN / T);
+      // C <= 8 (always for T = 256): slots staged in LDS; larger C up to the
+      // 64 slots of a block row stored per thread
+      constexpr int T = decltype(t)::value;
+      constexpr int CBIG = T == 256 ? 8 : kStagedSlots / (BigCfgW::BN / T);
       if (g.capacity <= 8)
         up_pack_bf16_wave<BigCfgW, T, 8, decltype(dbg)::value>
             <<<blocks, BigCfgW::NT, 0, s>>>(x, w_up_t, b_up, M, N, K, g.capacity, g.n_tiles,
@@ -1536,10 +1565,12 @@ hipError_t launch_up_pack_bf16(const Geometry& g, const uint16_t* x, const uint1
     };
     using I64 = std::integral_constant<int, 64>;
     using I128 = std::integral_constant<int, 128>;
+    using I256 = std::integral_constant<int, 256>;
     using Y = std::true_type;
     using No = std::false_type;
     if (g.tile == 64) hdbg ? go(I64{}, Y{}) : go(I64{}, No{});
-    else hdbg ? go(I128{}, Y{}) : go(I128{}, No{});
+    else if (g.tile == 128) hdbg ? go(I128{}, Y{}) : go(I128{}, No{});
+    else hdbg ? go(I256{}, Y{}) : go(I256{}, No{});
   } else if (M >= 128 && K % 64 == 0) {
     const int blocks = ((M + BigCfg::BM - 1) / BigCfg::BM) * ((N + BigCfg::BN - 1) / BigCfg::BN);
     up_pack_bf16_fast<BigCfg><<<blocks, BigCfg::NT, 0, s>>>(
