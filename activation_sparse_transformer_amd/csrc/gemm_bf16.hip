@@ -409,8 +409,11 @@ __device__ __forceinline__ void mainloop32_pipe(const uint16_t* __restrict__ A, 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = init[j];
-  // VALU writes of the accumulators, then MFMAs that read them (in asm)
-  asm volatile("s_nop 15\n\ts_nop 15" ::);
+  // VALU writes of the accumulators, then MFMAs that read them (in asm); the
+  // accumulators are operands so the writes cannot move past the wait
+  asm volatile("s_nop 15\n\ts_nop 15"
+               : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]),
+                 "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]));
   const uint16_t* asrc[CF::A_ISSUE];
   const uint16_t* bsrc[CF::B_ISSUE];
   dma_sources<CF::A_ISSUE, CF::NW>(A, lda, M, m0, asrc);
@@ -469,8 +472,11 @@ __device__ __forceinline__ void mainloop32_pipe(const uint16_t* __restrict__ A, 
     pipe_step(acc, f0, f1, a3);
   }
   pipe_last(acc, f1);
-  // MFMA results, then VALU reads of them (outside asm)
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::);
+  // MFMA results, then VALU reads of them (outside asm): the reads cannot move
+  // above the wait, which has the accumulators as operands
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15"
+               : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]),
+                 "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]));
   __syncthreads();  // operand stages are free for the epilogue
 }
 
