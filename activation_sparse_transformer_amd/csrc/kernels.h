@@ -100,6 +100,7 @@ struct RouteOut {
   int32_t* n_sparse;
   int32_t* status;
   const uint8_t* row_dense;
+  const int32_t* blk_cnt = nullptr;  // dense rows per block of row_or_kernel's rows
 };
 
 // The down-projection operands of a dense-row build that also runs the

@@ -60,12 +60,19 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// One thread per row: does any tile of the row overflow?
+// One thread per row: does any tile of the row overflow?  With `blk_cnt`,
+// each workgroup also stores how many of its kRowThreads rows are dense.
 __global__ __launch_bounds__(kRowThreads) void row_or_kernel(const uint8_t* __restrict__ flags,
                                                              int64_t N, int nt,
-                                                             uint8_t* __restrict__ row_dense) {
+                                                             uint8_t* __restrict__ row_dense,
+                                                             int32_t* __restrict__ blk_cnt) {
   const int64_t n = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
-  if (n < N) row_dense[n] = row_has_flag(flags + n * nt, nt) ? 1 : 0;
+  const bool d = n < N && row_has_flag(flags + n * nt, nt);
+  if (n < N) row_dense[n] = d ? 1 : 0;
+  if (blk_cnt != nullptr) {
+    const int c = __syncthreads_count(d);
+    if (threadIdx.x == 0) blk_cnt[blockIdx.x] = c;
+  }
 }
 
 // One workgroup: thread i takes a run of consecutive rows (with `flags`, it
@@ -189,16 +196,20 @@ __device__ int route_rows_in_block(const RouteOut& ro, const uint8_t* __restrict
   return ((mask >> n) & 1u) ? popc64(mask & ((uint64_t{1} << n) - 1u)) : -1;
 }
 
-// Routing once row_dense is known (row_or_kernel): workgroup n
-// counts the dense rows below row n itself (row_dense holds 0 or 1 per row, so
-// the popcount of each 16-byte piece counts them), writes its own entry of
-// the dense-row or the sparse-row list, and the last row's workgroup writes
-// the counts and the status word.  Returns the dense index of row n, or -1.
+// Routing once row_dense and the per-block dense counts are known
+// (row_or_kernel): workgroup n counts the dense rows below row n itself, as
+// the counts of the kRowThreads-row blocks below n's block plus the rows of
+// its own block below it (row_dense holds 0 or 1 per row, so the popcount of
+// each 16-byte piece counts them), writes its own entry of the dense-row or
+// the sparse-row list, and the last row's workgroup writes the counts and the
+// status word.  Returns the dense index of row n, or -1.
 __device__ int route_rows_prefix(const RouteOut& ro, int64_t cap, int64_t n) {
   __shared__ int s_part[1024 / kWave];  // up to 1024 threads
   const uint8_t* rd = ro.row_dense;
+  const int64_t b = n / kRowThreads, r0 = b * kRowThreads;
   int c = 0;
-  for (int64_t i = static_cast<int64_t>(threadIdx.x) * 16; i < n;
+  for (int64_t i = threadIdx.x; i < b; i += blockDim.x) c += ro.blk_cnt[i];
+  for (int64_t i = r0 + static_cast<int64_t>(threadIdx.x) * 16; i < n;
        i += static_cast<int64_t>(blockDim.x) * 16) {
     if (i + 16 <= n) {
       const uint4 v = *reinterpret_cast<const uint4*>(rd + i);
@@ -509,7 +520,8 @@ hipError_t launch_route_scan(const Geometry& g, const RouteBufs& rb, int32_t* de
   const bool fused = g.n_rows <= kScanThreads;
   if (!fused) {
     const unsigned blocks = static_cast<unsigned>((g.n_rows + kRowThreads - 1) / kRowThreads);
-    row_or_kernel<<<blocks, kRowThreads, 0, s>>>(rb.flags, g.n_rows, g.n_tiles, rb.row_dense);
+    row_or_kernel<<<blocks, kRowThreads, 0, s>>>(rb.flags, g.n_rows, g.n_tiles, rb.row_dense,
+                                                 nullptr);
   }
   route_scan_kernel<<<1, kScanThreads, 0, s>>>(fused ? rb.flags : nullptr, g.n_tiles, rb.row_dense, g.n_rows,
                                                rb.row_map, dense_rows, dense_cap, n_dense,
@@ -534,10 +546,12 @@ hipError_t launch_route_materialize(const Geometry& g, int elem_bytes, const Rou
   if (mode == 0) return hipErrorInvalidValue;
   if (mode == 2) {
     const unsigned blocks = static_cast<unsigned>((g.n_rows + kRowThreads - 1) / kRowThreads);
-    row_or_kernel<<<blocks, kRowThreads, 0, s>>>(rb.flags, g.n_rows, g.n_tiles, rb.row_dense);
+    // the row map is not used in this mode: its first entries hold the per-block counts
+    row_or_kernel<<<blocks, kRowThreads, 0, s>>>(rb.flags, g.n_rows, g.n_tiles, rb.row_dense,
+                                                 rb.row_map);
   }
   const RouteOut ro{g.n_rows, dense_rows, n_dense, rb.sparse_rows, rb.n_sparse, status,
-                    mode == 2 ? rb.row_dense : nullptr};
+                    mode == 2 ? rb.row_dense : nullptr, mode == 2 ? rb.row_map : nullptr};
   return launch_materialize(g, elem_bytes, nullptr, rb.flags, spill, full_src, vals, idx, cnt,
                             dense_values, dense_cap, s, &ro, sp);
 }
