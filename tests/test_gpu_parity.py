@@ -380,10 +380,10 @@ def test_forward_fp32_many_rows(n, dm, dff):
 @pytest.mark.parametrize("n,dm,dff,C", [(300, 256, 1024, 4), (260, 128, 1280, 16), (130, 192, 768, 17),
                                          (129, 64, 576, 4)])
 def test_forward_tile64_bf16(n, dm, dff, C):
-    """bf16 with T = 64: the up-projection's waves own whole tiles (2 per wave)
-    up to 64 staged slots per block row (C <= 16); C = 17 and a d_ff that is
-    not a multiple of 128 take the other epilogue.  Pack bit-exact, h and y
-    within tolerance."""
+    """bf16 with T = 64: the LDS pack epilogue with slots staged (C <= 8) or
+    stored per thread (C = 16, up to 64 slots per block row); C = 17 takes
+    the other epilogue; d_ff = 576 (9 tiles) leaves the last block's columns
+    past d_ff unused.  Pack bit-exact, h and y within tolerance."""
     cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n, d_model=dm, d_ff=dff, tile=64, capacity=C)
     say(f"forward bf16 T=64 n={n} dm={dm} dff={dff} C={C}")
     t = make_inputs(cfg)
