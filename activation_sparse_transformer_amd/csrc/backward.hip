@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kBwdScanThreads) void bwd_offsets_kernel(
 // shuffles, UP passes of gathers in flight), lane l of a group holding slice
 // columns (v * P + l) * V.. for v < NVL.  The groups' sums are added in a
 // fixed butterfly order at the end, so every result is a fixed function of
-// the input.  part[entry][s] holds the slices' partial dots of dz.
+// the input.  part[s * pstride + entry] holds slice s's partial dot of dz.
 
 // A lane's columns of one slice of an fp32 gradient row: acc, or zeros when
 // acc is null.
@@ -335,13 +335,13 @@ __device__ __forceinline__ void up_step(int e0, int cnt, const int4& mine, uint3
 }
 
 // Pass A: for each entry (row n, h) of neuron j, the partial dot of dy[n]
-// with W_down[j] over the slice, stored at part[entry][s]; and
+// with W_down[j] over the slice, stored at part[s * pstride + entry]; and
 // dW_down[j][slice] = sum of h * dy[n][slice].
 template <typename E, int P, int NVL>
 __global__ __launch_bounds__(kBwdThreads) void bwd_slice_down_kernel(
     const int32_t* __restrict__ offsets, const int4* __restrict__ ents, const E* __restrict__ dy,
     const E* __restrict__ w_down, int dff, int dm, int S, int sw, float* __restrict__ part,
-    float* __restrict__ dw_down) {
+    int64_t pstride, float* __restrict__ dw_down) {
   constexpr int V = 16 / sizeof(E);
   constexpr int GPW = kWave / P;                              // entries per pass
   constexpr int UP = GPW * NVL >= 8 ? 1 : 8 / (GPW * NVL);  // passes in flight
@@ -381,7 +381,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_slice_down_kernel(
       down_step<E, P, NVL, UP, false>(e0, cnt, mine, dy, dm, col, wv, acc, mypd);
     for (; e0 < cnt; e0 += GPW)
       down_step<E, P, NVL, 1, true>(e0, cnt, mine, dy, dm, col, wv, acc, mypd);
-    if (lane < cnt) part[static_cast<int64_t>(b + base + lane) * S + s] = mypd;
+    // slice-major: the chunk's partials are one coalesced store
+    if (lane < cnt) part[s * pstride + b + base + lane] = mypd;
   }
 #pragma unroll
   for (int o = P; o < kWave; o <<= 1)
@@ -397,7 +398,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_slice_down_kernel(
 template <typename E, int P, int NVL>
 __global__ __launch_bounds__(kBwdThreads) void bwd_slice_up_kernel(
     const int32_t* __restrict__ offsets, const int4* __restrict__ ents, const E* __restrict__ x,
-    const float* __restrict__ part, int dff, int dm, int S, int sw, int64_t sparse_slots,
+    const float* __restrict__ part, int64_t pstride, int dff, int dm, int S, int sw,
+    int64_t sparse_slots,
     E* __restrict__ dz_vals, E* __restrict__ dz_dense, float* __restrict__ dw_up_t,
     float* __restrict__ db) {
   typedef ElemTraits<E> Tr;
@@ -432,13 +434,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_slice_up_kernel(
     const int64_t me = b + base + min(lane, cnt - 1);
     const int4 mine = ents[me];
     float d;
-    if (S == 8) {  // the 8 partials are 32 contiguous bytes: two loads, added in slice order
-      const float4 p0 = *reinterpret_cast<const float4*>(part + me * 8);
-      const float4 p1 = *reinterpret_cast<const float4*>(part + me * 8 + 4);
-      d = ((((((p0.x + p0.y) + p0.z) + p0.w) + p1.x) + p1.y) + p1.z) + p1.w;
+    if (S == 8) {  // the 8 partials, each load coalesced over the lanes, added in slice order
+      float p[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) p[t] = part[t * pstride + me];
+      d = ((((((p[0] + p[1]) + p[2]) + p[3]) + p[4]) + p[5]) + p[6]) + p[7];
     } else {
-      d = part[me * S];
-      for (int t = 1; t < S; ++t) d += part[me * S + t];
+      d = part[me];
+      for (int t = 1; t < S; ++t) d += part[t * pstride + me];
     }
     const E dze = Tr::from_f32(d);
     const float dzf = lane < cnt ? Tr::to_f32(dze) : 0.f;
@@ -513,11 +516,12 @@ hipError_t launch_slices(const Geometry& g, const SlicePlan& sp, const BwdWorksp
       static_cast<unsigned>((g.d_ff + kBwdWaves - 1) / kBwdWaves) * static_cast<unsigned>(sp.S);
   bwd_slice_down_kernel<E, P, NVL><<<blocks, kBwdThreads, 0, s>>>(
       w.offsets, w.ents, static_cast<const E*>(dy), static_cast<const E*>(w_down), g.d_ff,
-      g.d_model, sp.S, sp.sw, w.part_dz, dw_down);
+      g.d_model, sp.S, sp.sw, w.part_dz, w.part_stride, dw_down);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   bwd_slice_up_kernel<E, P, NVL><<<blocks, kBwdThreads, 0, s>>>(
-      w.offsets, w.ents, static_cast<const E*>(x), w.part_dz, g.d_ff, g.d_model, sp.S, sp.sw,
+      w.offsets, w.ents, static_cast<const E*>(x), w.part_dz, w.part_stride, g.d_ff, g.d_model,
+      sp.S, sp.sw,
       g.n_rows * g.n_tiles * g.capacity, static_cast<E*>(w.dz_vals),
       static_cast<E*>(w.dz_dense), dw_up_t, db);
   return hipGetLastError();
@@ -578,6 +582,7 @@ BwdWorkspace bwd_carve(const Geometry& g, int elem_bytes, int64_t dense_cap, voi
   w.ents = static_cast<int4*>(take(ents * sizeof(int4)));
   const SlicePlan sp = bwd_slice_plan(g.d_model, elem_bytes);
   w.part_dz = static_cast<float*>(take(static_cast<size_t>(sp.S) * ents * sizeof(float)));
+  w.part_stride = static_cast<int64_t>(ents);
   w.part = p == nullptr ? nullptr : reinterpret_cast<float*>(p + ent_off);
   w.part_elems = static_cast<int64_t>((off - ent_off) / 4);
   const size_t sk = skinny_ws_bytes(g);

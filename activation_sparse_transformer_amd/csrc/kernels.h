@@ -241,7 +241,8 @@ struct BwdWorkspace {
   int32_t* ncount;              // [d_ff] entries per neuron
   int32_t* offsets;             // [d_ff + 1] first entry of each neuron
   int4* ents;                   // [entries] {row, h as f32 bits, slot, 0}, by neuron then row
-  float* part_dz;               // [entries][S] partial dots of dz per column slice
+  float* part_dz;               // [S][part_stride] partial dots of dz per column slice
+  int64_t part_stride;          // entries per slice of part_dz
   float* part;                  // the entry area, reused for the fallback's partial sums
   int64_t part_elems;
   float* skinny;                // skinny_ws_bytes(g) or nullptr
