@@ -563,12 +563,17 @@ def test_forward_fp32_small_batch_matches_timed_and_standalone(n_rows, d_model, 
     assert_close_rel(as_f64(y2), y_ref, TOL[cfg.torch_dtype], "twell_spmm y")
 
 
-@pytest.mark.parametrize("n_rows", [16, 48, 700, 1500, 2600])
-def test_forward_timed_variant_matches_plain_call(n_rows):
+@pytest.mark.parametrize("n_rows,d_model,d_ff", [(16, 512, 2048), (48, 512, 2048),
+                                                 (700, 512, 2048), (1500, 512, 2048),
+                                                 (2600, 512, 2048), (1100, 2048, 8192),
+                                                 (3000, 1024, 4096)])
+def test_forward_timed_variant_matches_plain_call(n_rows, d_model, d_ff):
     """The event-recording variant (every stage in its own launches) and the
     plain call (at most 64 rows: the sparse product inside the fallback's
-    split-K launch) give the same y and hybrid, bit for bit."""
-    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=512, d_ff=2048)
+    split-K launch) give the same y and hybrid, bit for bit; past 1024 rows
+    with one, two and four XCD column slices of the sparse product."""
+    cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=n_rows, d_model=d_model, d_ff=d_ff)
+    say(f"timed vs plain n={n_rows} dm={d_model} dff={d_ff}")
     t = make_inputs(cfg)
     d = inputs_to_device(t)
     a = twell.ffn_sparse_forward(d["x"], d["w_up_t"], d["b_up"], d["w_down"], cfg.tile,
