@@ -1332,11 +1332,14 @@ __global__ __launch_bounds__(CF::NT) void fallback_bf16_fast(
     }
 }
 
-// Sum of the fallback's K slices (when fallback_bf16_fast split K): thread i
-// adds 8 consecutive outputs of one live row over the slices in slice order,
-// rounds them and stores them to y[dense_rows[m]].  Launched for the worst
-// case; with S = 1 every workgroup leaves at once.
+// Sum of the fallback's K slices (when fallback_bf16_fast split K): work
+// item i adds 8 consecutive outputs of one live row over the slices in slice
+// order, rounds them and stores them to y[dense_rows[m]].  The grid is capped
+// and strides over the live rows' items, so a few live rows do not pay for a
+// worst-case grid of workgroups that only leave; with S = 1 every workgroup
+// leaves at once.
 constexpr int kFbReduceThreads = 256;
+constexpr int kFbReduceGrid = 1024;
 
 __global__ __launch_bounds__(kFbReduceThreads) void fallback_reduce_kernel(
     const float* __restrict__ part, int64_t part_elems, const int32_t* __restrict__ n_dense,
@@ -1347,27 +1350,42 @@ __global__ __launch_bounds__(kFbReduceThreads) void fallback_reduce_kernel(
   const FbSplit sp = fb_split(M, BM, n_blocks, split_grid, K / fast::BKF, N, part, part_elems);
   if (M <= 0 || sp.slices == 1) return;
   const int per_row = N / 8;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kFbReduceThreads + threadIdx.x;
-  if (i >= static_cast<int64_t>(M) * per_row) return;
-  const int m = static_cast<int>(i / per_row);
-  const int c = static_cast<int>(i % per_row) * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int64_t items = static_cast<int64_t>(M) * per_row;
   const int64_t slice_stride = static_cast<int64_t>(M) * N;
-  const float* src = part + static_cast<int64_t>(m) * N + c;
-  for (int s = 0; s < sp.slices; ++s) {
-    const float4 a = *reinterpret_cast<const float4*>(src + s * slice_stride);
-    const float4 b = *reinterpret_cast<const float4*>(src + s * slice_stride + 4);
-    acc[0] += a.x, acc[1] += a.y, acc[2] += a.z, acc[3] += a.w;
-    acc[4] += b.x, acc[5] += b.y, acc[6] += b.z, acc[7] += b.w;
-  }
-  const int64_t yrow = dense_rows[m];
-  if (yrow < 0 || yrow >= y_rows) return;  // never write outside y
-  uint32_t o[4];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFbReduceThreads + threadIdx.x; i < items;
+       i += static_cast<int64_t>(gridDim.x) * kFbReduceThreads) {
+    const int m = static_cast<int>(i / per_row);
+    const int c = static_cast<int>(i % per_row) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float* src = part + static_cast<int64_t>(m) * N + c;
+    auto add = [&](const float4& a, const float4& b) {
+      acc[0] += a.x, acc[1] += a.y, acc[2] += a.z, acc[3] += a.w;
+      acc[4] += b.x, acc[5] += b.y, acc[6] += b.z, acc[7] += b.w;
+    };
+    int s = 0;
+    // 8 slices' loads in flight at once (many slices come from few live rows)
+    for (; s + 8 <= sp.slices; s += 8) {
+      float4 a[8], b[8];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    o[q] = static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * q])) |
-           (static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * q + 1])) << 16);
-  *reinterpret_cast<uint4*>(y + yrow * N + c) = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int u = 0; u < 8; ++u) {
+        a[u] = *reinterpret_cast<const float4*>(src + (s + u) * slice_stride);
+        b[u] = *reinterpret_cast<const float4*>(src + (s + u) * slice_stride + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) add(a[u], b[u]);
+    }
+    for (; s < sp.slices; ++s)
+      add(*reinterpret_cast<const float4*>(src + s * slice_stride),
+          *reinterpret_cast<const float4*>(src + s * slice_stride + 4));
+    const int64_t yrow = dense_rows[m];
+    if (yrow < 0 || yrow >= y_rows) continue;  // never write outside y
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * q])) |
+             (static_cast<uint32_t>(ElemTraits<uint16_t>::from_f32(acc[2 * q + 1])) << 16);
+    *reinterpret_cast<uint4*>(y + yrow * N + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 // ------------------------------------------------- skinny split-K (bf16, <= 64 rows)
@@ -1630,8 +1648,8 @@ hipError_t launch_fallback_bf16(const Geometry& g, const uint16_t* dense_values,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || part == nullptr) return e;
     const int64_t outs = worst * (N / 8);
-    const unsigned rblocks =
-        static_cast<unsigned>((outs + kFbReduceThreads - 1) / kFbReduceThreads);
+    const int64_t want = (outs + kFbReduceThreads - 1) / kFbReduceThreads;
+    const unsigned rblocks = static_cast<unsigned>(want < kFbReduceGrid ? want : kFbReduceGrid);
     fallback_reduce_kernel<<<rblocks, kFbReduceThreads, 0, s>>>(
         part, part_elems, n_dense, dense_cap, dense_rows, y, g.n_rows, N, K, MidCfg::BM,
         MidCfg::BN, grid);
