@@ -125,8 +125,8 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
 // G2 without the scan kernel: route_mode says whether the dense-row build can
 // route the rows itself (1: at most 64 rows, each workgroup ORs every row's
 // tile flags and numbers the dense rows with one ballot; 2: more than 1024
-// and at most 16384 rows, row_or_kernel first, then each workgroup counts the
-// dense rows below its row from row_dense) or not (0).  Writes what
+// and at most 16384 rows, row_or_kernel first, then the build numbers the
+// dense rows from row_dense and the per-block dense counts) or not (0).  Writes what
 // launch_route_scan and launch_materialize write, except row_map (and, in mode
 // 1, row_dense).  full_src: h when the rows are copied from it (twell_pack).
 int route_mode(const Geometry& g);

@@ -31,6 +31,9 @@ namespace {
 constexpr int kScanThreads = 1024;
 constexpr int kRowThreads = 256;
 constexpr int64_t kPrefixMaxRows = 16384;
+// Workgroups of the listed dense-row build (at most one per row; measured at
+// 1853 dense rows of 4096: 2048 and 4096 alike, 1024 0.4 us slower).
+constexpr int64_t kListedGrid = 2048;
 
 __device__ __forceinline__ bool row_has_flag(const uint8_t* __restrict__ f, int nt) {
   uint32_t any = 0;
@@ -253,43 +256,17 @@ __device__ __forceinline__ int row_dense_index(const RouteOut& ro, const int32_t
   else return row_map[n];
 }
 
-// One workgroup per row.  A dense row is assembled in LDS (zeros, then the
-// stored slots scattered in), then written out 16 bytes per thread, taking the
-// overflowing tiles from the spill area; with `full_src` the row is copied
-// from h as is.  Finally the row's TwELL slots are cleared.
-//
-// With `sp.w_down` set (float32, rows routed in the workgroup, built in LDS,
-// 1024 threads), a sparse row's workgroup computes the row's y instead of
-// leaving: its 16 waves take the row's 16 tile ranges, as the separate few-row
-// sparse kernel does, so y is the same bits.  sp_dm, sp_tpw, sp_chunks:
-// d_model, tiles per range, 64-lane column chunks.
-template <typename E, bool IN_LDS, int RM, int NT = kRowThreads>
-__global__ __launch_bounds__(NT) void materialize_kernel(
-    int dff, int T, int C, int nt, const int32_t* __restrict__ row_map,
-    const uint8_t* __restrict__ flags, const E* __restrict__ spill, const E* __restrict__ full_src,
-    E* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
-    E* __restrict__ dense_values, int64_t cap, RouteOut ro, BuildSpmm sp, int sp_dm, int sp_tpw,
-    int sp_chunks) {
+// Dense row n, the m-th: when m < cap, its dense_values row is written from
+// full_src, or rebuilt from the row's slots and spilled tiles (in the LDS row
+// buffer `rowbuf` when IN_LDS); then the row's TwELL slots are cleared.
+// Every thread of the workgroup takes part; it ends on no barrier.
+template <typename E, bool IN_LDS, int NT>
+__device__ __forceinline__ void build_dense_row(
+    int64_t n, int m, E* rowbuf, int dff, int T, int C, int nt, const uint8_t* __restrict__ flags,
+    const E* __restrict__ spill, const E* __restrict__ full_src, E* __restrict__ vals,
+    uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt, E* __restrict__ dense_values,
+    int64_t cap) {
   constexpr int V = Vec16<E>::N;
-  extern __shared__ __attribute__((aligned(16))) unsigned char mat_lds[];
-  E* rowbuf = reinterpret_cast<E*>(mat_lds);
-  const int64_t n = blockIdx.x;
-  const int m = row_dense_index<RM>(ro, row_map, flags, nt, cap, n);
-  if (m < 0) {
-    if constexpr (IN_LDS && RM == 1 && NT == kSplitParts * kWave &&
-                  std::is_same<E, float>::value) {
-      if (sp.w_down != nullptr) {
-        uint2* lists = reinterpret_cast<uint2*>(mat_lds);
-        float* red = reinterpret_cast<float*>(lists + kSplitParts * sp_tpw * C);
-        for (int chunk = 0; chunk < sp_chunks; ++chunk)
-          spmm_split_row_chunk<E, kSplitParts, 1>(vals, idx, cnt, n,
-                                                  static_cast<const E*>(sp.w_down),
-                                                  static_cast<E*>(sp.y), sp_dm, T, C, nt, sp_tpw,
-                                                  chunk, lists, red);
-      }
-    }
-    return;
-  }
   const int64_t slot0 = n * nt;
   const int nslots = nt * C;
   if (m < cap) {
@@ -344,6 +321,136 @@ __global__ __launch_bounds__(NT) void materialize_kernel(
     idx[slot0 * C + i] = 0;
   }
   for (int i = threadIdx.x; i < nt; i += NT) cnt[slot0 + i] = 0;
+}
+
+// One workgroup per row.  A dense row is assembled in LDS (zeros, then the
+// stored slots scattered in), then written out 16 bytes per thread, taking the
+// overflowing tiles from the spill area; with `full_src` the row is copied
+// from h as is.  Finally the row's TwELL slots are cleared.
+//
+// With `sp.w_down` set (float32, rows routed in the workgroup, built in LDS,
+// 1024 threads), a sparse row's workgroup computes the row's y instead of
+// leaving: its 16 waves take the row's 16 tile ranges, as the separate few-row
+// sparse kernel does, so y is the same bits.  sp_dm, sp_tpw, sp_chunks:
+// d_model, tiles per range, 64-lane column chunks.
+template <typename E, bool IN_LDS, int RM, int NT = kRowThreads>
+__global__ __launch_bounds__(NT) void materialize_kernel(
+    int dff, int T, int C, int nt, const int32_t* __restrict__ row_map,
+    const uint8_t* __restrict__ flags, const E* __restrict__ spill, const E* __restrict__ full_src,
+    E* __restrict__ vals, uint8_t* __restrict__ idx, uint8_t* __restrict__ cnt,
+    E* __restrict__ dense_values, int64_t cap, RouteOut ro, BuildSpmm sp, int sp_dm, int sp_tpw,
+    int sp_chunks) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char mat_lds[];
+  E* rowbuf = reinterpret_cast<E*>(mat_lds);
+  const int64_t n = blockIdx.x;
+  const int m = row_dense_index<RM>(ro, row_map, flags, nt, cap, n);
+  if (m < 0) {
+    if constexpr (IN_LDS && RM == 1 && NT == kSplitParts * kWave &&
+                  std::is_same<E, float>::value) {
+      if (sp.w_down != nullptr) {
+        uint2* lists = reinterpret_cast<uint2*>(mat_lds);
+        float* red = reinterpret_cast<float*>(lists + kSplitParts * sp_tpw * C);
+        for (int chunk = 0; chunk < sp_chunks; ++chunk)
+          spmm_split_row_chunk<E, kSplitParts, 1>(vals, idx, cnt, n,
+                                                  static_cast<const E*>(sp.w_down),
+                                                  static_cast<E*>(sp.y), sp_dm, T, C, nt, sp_tpw,
+                                                  chunk, lists, red);
+      }
+    }
+    return;
+  }
+  build_dense_row<E, IN_LDS, NT>(n, m, rowbuf, dff, T, C, nt, flags, spill, full_src, vals, idx,
+                                  cnt, dense_values, cap);
+}
+
+// Routing and dense-row build once row_dense and the per-block dense counts
+// are known (row_or_kernel), with workgroups for the dense rows only:
+// * every workgroup adds up the blocks' counts (one wave scan) into the
+//   offsets of each kRowThreads-row block's dense rows;
+// * workgroup b < (row blocks) writes block b's entries of the dense-row and
+//   sparse-row lists (a ballot prefix over the block's row flags), and the
+//   last block's workgroup the counts and the status word;
+// * workgroup b then builds dense rows b, b + G, ... of the n_dense, finding
+//   the m-th dense row from the block offsets and a ballot over that block's
+//   row flags.
+// The lists and dense_values are the same as the one-workgroup-per-row build
+// writes; only workgroups that have a dense row to build or a block to list
+// do more than read the counts.
+template <typename E, bool IN_LDS>
+__global__ __launch_bounds__(kRowThreads) void materialize_listed_kernel(
+    int dff, int T, int C, int nt, const uint8_t* __restrict__ flags, const E* __restrict__ spill,
+    const E* __restrict__ full_src, E* __restrict__ vals, uint8_t* __restrict__ idx,
+    uint8_t* __restrict__ cnt, E* __restrict__ dense_values, int64_t cap, RouteOut ro) {
+  static_assert(kRowThreads == 4 * kWave, "four waves per workgroup");
+  constexpr int kMaxBlocks = static_cast<int>(kPrefixMaxRows / kRowThreads);
+  static_assert(kMaxBlocks <= kWave, "one wave scans the block counts");
+  extern __shared__ __attribute__((aligned(16))) unsigned char mat_lds[];
+  __shared__ int s_off[kMaxBlocks + 1];
+  __shared__ int s_wave[kRowThreads / kWave];
+  __shared__ int s_blk;
+  __shared__ int64_t s_row;
+  const int64_t N = ro.n_rows;
+  const int nb = static_cast<int>((N + kRowThreads - 1) / kRowThreads);
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  if (wave == 0) {
+    int c = lane < nb ? ro.blk_cnt[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int u = __shfl_up(c, o, kWave);
+      if (lane >= o) c += u;
+    }
+    if (lane == 0) s_off[0] = 0;
+    if (lane < nb) s_off[lane + 1] = c;  // inclusive: offsets of the blocks above
+  }
+  __syncthreads();
+  const int n_dense = s_off[nb];
+  // the rank of each row's flag among the dense rows of its block below it
+  auto block_rank = [&](int64_t r0, bool& d) {
+    const int64_t r = r0 + threadIdx.x;
+    d = r < N && ro.row_dense[r] != 0;
+    const uint64_t bal = wave_ballot(d);
+    if (lane == 0) s_wave[wave] = popc64(bal);
+    __syncthreads();
+    int below = popc_below(bal);
+    for (int w = 0; w < wave; ++w) below += s_wave[w];
+    return below;
+  };
+  if (static_cast<int>(blockIdx.x) < nb) {
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * kRowThreads;
+    bool d;
+    const int m = s_off[blockIdx.x] + block_rank(r0, d);
+    const int64_t r = r0 + threadIdx.x;
+    if (r < N) {
+      if (d) {
+        if (m < cap) ro.dense_rows[m] = static_cast<int32_t>(r);
+      } else {
+        ro.sparse_rows[r - m] = static_cast<int32_t>(r);
+      }
+    }
+    if (static_cast<int>(blockIdx.x) == nb - 1 && threadIdx.x == 0) {
+      *ro.n_dense = n_dense;
+      *ro.n_sparse = static_cast<int32_t>(N - n_dense);
+      if (ro.status != nullptr) *ro.status = n_dense > cap ? TWELL_ERR_DENSE_CAPACITY : TWELL_OK;
+    }
+    __syncthreads();  // s_wave is reused below
+  }
+  for (int m = blockIdx.x; m < n_dense; m += gridDim.x) {
+    // the block holding the m-th dense row, then the row within it
+    if (threadIdx.x == 0) s_row = -1;
+    if (threadIdx.x < nb && s_off[threadIdx.x] <= m && m < s_off[threadIdx.x + 1])
+      s_blk = threadIdx.x;
+    __syncthreads();
+    const int b = s_blk;
+    bool d;
+    const int k = block_rank(static_cast<int64_t>(b) * kRowThreads, d);
+    if (d && k == m - s_off[b]) s_row = static_cast<int64_t>(b) * kRowThreads + threadIdx.x;
+    __syncthreads();
+    if (s_row < 0) break;  // (never: the counts come from the same flags)
+    build_dense_row<E, IN_LDS, kRowThreads>(s_row, m, reinterpret_cast<E*>(mat_lds), dff, T, C,
+                                            nt, flags, spill, full_src, vals, idx, cnt,
+                                            dense_values, cap);
+    __syncthreads();  // s_blk, s_row, s_wave and the row buffer are reused
+  }
 }
 
 // Dense-row build for capacities of 4 or 8 slots: one workgroup per row,
@@ -649,6 +756,27 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   }
   const bool in_lds = full_src == nullptr && row_bytes <= 64 * 1024;
   const size_t lds = in_lds ? row_bytes : 0;
+  if (rmode == 2) {
+    // workgroups for the row blocks' lists and the dense rows only
+    const int64_t nb = (g.n_rows + kRowThreads - 1) / kRowThreads;
+    const int64_t want = g.n_rows < kListedGrid ? g.n_rows : kListedGrid;
+    const unsigned lblocks = static_cast<unsigned>(want > nb ? want : nb);
+    auto listed = [&](auto tag, auto lds_tag) {
+      typedef decltype(tag) E;
+      materialize_listed_kernel<E, decltype(lds_tag)::value><<<lblocks, kRowThreads, lds, s>>>(
+          g.d_ff, g.tile, g.capacity, g.n_tiles, flags, static_cast<const E*>(spill),
+          static_cast<const E*>(full_src), static_cast<E*>(vals), idx, cnt,
+          static_cast<E*>(dense_values), dense_cap, ro);
+    };
+    typedef std::integral_constant<bool, true> InLds;
+    typedef std::integral_constant<bool, false> NotInLds;
+    if (elem_bytes == 2) {
+      if (in_lds) listed(uint16_t{}, InLds{}); else listed(uint16_t{}, NotInLds{});
+    } else {
+      if (in_lds) listed(float{}, InLds{}); else listed(float{}, NotInLds{});
+    }
+    return hipGetLastError();
+  }
   auto go = [&](auto tag, auto lds_tag, auto route_tag) {
     typedef decltype(tag) E;
     materialize_kernel<E, decltype(lds_tag)::value, decltype(route_tag)::value>
@@ -660,9 +788,8 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   };
   typedef std::integral_constant<bool, true> Yes;
   typedef std::integral_constant<bool, false> No;
-  auto by_route = [&](auto tag, auto lds_tag) {
+  auto by_route = [&](auto tag, auto lds_tag) {  // (route mode 2 returned above)
     if (rmode == 1) go(tag, lds_tag, std::integral_constant<int, 1>{});
-    else if (rmode == 2) go(tag, lds_tag, std::integral_constant<int, 2>{});
     else go(tag, lds_tag, std::integral_constant<int, 0>{});
   };
   auto by_lds = [&](auto tag) {
