@@ -104,6 +104,21 @@ size_t fwd_ws_bytes(const twell_shape* s) {
          align_up(skinny_ws_bytes(geometry(s)));
 }
 
+// twell_spmm's optional workspace: the split-K kernels' partial sums for at
+// most 64 rows; for bf16 beyond that, room for 32 K slices of every row, at
+// most 32 MiB (the 128 x 128 tile kernel's 512 workgroups never hold more:
+// slices x live tiles <= 512, 64 KiB of partial sums each).
+size_t spmm_ws_bytes(const twell_shape* s) {
+  const Geometry g = geometry(s);
+  size_t b = skinny_ws_bytes(g);
+  if (s->dtype == TWELL_BF16 && b == 0) {
+    const size_t all = size_t{32} * static_cast<size_t>(s->n_rows) *
+                       static_cast<size_t>(s->d_model) * sizeof(float);
+    b = align_up(all < (size_t{32} << 20) ? all : (size_t{32} << 20));
+  }
+  return b;
+}
+
 // Floats that fit in the forward's spill area [N][d_ff] of dtype.
 int64_t spill_floats(const twell_shape* s) {
   return static_cast<int64_t>(s->n_rows) * s->d_ff * elem_bytes(s->dtype) / 4;
@@ -427,14 +442,20 @@ TWELL_EXPORT int twell_unpack(const twell_shape* shape, const twell_hybrid* in, 
                                   in->dense_capacity, h, static_cast<hipStream_t>(stream)));
 }
 
+TWELL_EXPORT size_t twell_spmm_workspace_size(const twell_shape* shape) {
+  if (check_shape(shape, true) != TWELL_OK) return 0;
+  return spmm_ws_bytes(shape);
+}
+
 TWELL_EXPORT int twell_spmm(const twell_shape* shape, const twell_hybrid* in, const void* w_down,
-                            void* y, void* stream) {
+                            void* y, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_shape(shape, true);
   if (rc != TWELL_OK) return rc;
   const Geometry g = geometry(shape);
   if ((rc = check_hybrid(in, g.n_rows)) != TWELL_OK) return rc;
   if (g.n_rows > 0 && (w_down == nullptr || y == nullptr)) return TWELL_ERR_INVALID_ARG;
-  if (!aligned16(w_down) || !aligned16(y)) return TWELL_ERR_INVALID_ARG;
+  if (!aligned16(w_down) || !aligned16(y) || !aligned16(workspace)) return TWELL_ERR_INVALID_ARG;
+  if (workspace != nullptr && workspace_bytes < spmm_ws_bytes(shape)) return TWELL_ERR_WORKSPACE;
   if (g.n_rows == 0) return TWELL_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int eb = elem_bytes(shape->dtype);
@@ -442,16 +463,22 @@ TWELL_EXPORT int twell_spmm(const twell_shape* shape, const twell_hybrid* in, co
   const DenseSkip skip{in->dense_rows, in->n_dense, in->dense_capacity};
   TWELL_TRY(launch_spmm_sparse(g, eb, in->values, in->indices, in->counts, nullptr, nullptr,
                                in->dense_capacity > 0 ? &skip : nullptr, w_down, y, st));
-  // ... and the stored dense rows by the dense fallback GEMM
+  // ... and the stored dense rows by the dense fallback GEMM, splitting K
+  // over the workspace's partial sums when there is one
+  float* ws = workspace != nullptr && spmm_ws_bytes(shape) > 0 ? static_cast<float*>(workspace)
+                                                              : nullptr;
+  float* skinny = ws != nullptr && skinny_ws_bytes(g) > 0 ? ws : nullptr;
   if (eb == 2)
     TWELL_TRY(launch_fallback_bf16(g, static_cast<const uint16_t*>(in->dense_values),
                                    in->dense_rows, in->n_dense, in->dense_capacity,
                                    static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(y),
-                                   st));
+                                   st, skinny, ws,
+                                   ws != nullptr ? static_cast<int64_t>(workspace_bytes / 4) : 0));
   else
     TWELL_TRY(launch_fallback_f32(g, static_cast<const float*>(in->dense_values), in->dense_rows,
                                   in->n_dense, in->dense_capacity,
-                                  static_cast<const float*>(w_down), static_cast<float*>(y), st));
+                                  static_cast<const float*>(w_down), static_cast<float*>(y), st,
+                                  skinny));
   return TWELL_OK;
 }
 

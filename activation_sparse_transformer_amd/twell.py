@@ -31,7 +31,8 @@ _DTYPE_CODE = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTS = (
     "twell_version", "twell_status_string", "ffn_sparse_workspace_size", "ffn_sparse_forward",
     "ffn_sparse_forward_events", "twell_pack_workspace_size", "twell_pack", "twell_pack_noalloc",
-    "twell_unpack", "twell_spmm", "ell_pack_workspace_size", "ell_pack", "ell_unpack", "ell_spmm",
+    "twell_unpack", "twell_spmm", "twell_spmm_workspace_size", "ell_pack_workspace_size",
+    "ell_pack", "ell_unpack", "ell_spmm",
     "ffn_sparse_backward_workspace_size", "ffn_sparse_backward", "ffn_sparse_gated_forward",
 )
 
@@ -94,7 +95,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.twell_pack.argtypes, lib.twell_pack.restype = [S, P, H, P, sz, P, P], I
     lib.twell_pack_noalloc.argtypes, lib.twell_pack_noalloc.restype = [S, P, H, P, P], I
     lib.twell_unpack.argtypes, lib.twell_unpack.restype = [S, H, P, P], I
-    lib.twell_spmm.argtypes, lib.twell_spmm.restype = [S, H, P, P, P], I
+    lib.twell_spmm.argtypes, lib.twell_spmm.restype = [S, H, P, P, P, sz, P], I
+    lib.twell_spmm_workspace_size.argtypes, lib.twell_spmm_workspace_size.restype = [S], sz
     E = ctypes.POINTER(EllStruct)
     lib.ell_pack_workspace_size.argtypes, lib.ell_pack_workspace_size.restype = [S], sz
     lib.ell_pack.argtypes, lib.ell_pack.restype = [S, P, E, P, sz, P, P], I
@@ -381,8 +383,14 @@ def twell_unpack(hy: Hybrid, out: Optional[torch.Tensor] = None) -> torch.Tensor
     return out
 
 
-def twell_spmm(hy: Hybrid, w_down: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The hybrid down-projection y [N, d_model] = unpack(hy) @ w_down."""
+def twell_spmm(hy: Hybrid, w_down: torch.Tensor, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, use_workspace: bool = True
+               ) -> torch.Tensor:
+    """The hybrid down-projection y [N, d_model] = unpack(hy) @ w_down.
+
+    With `use_workspace` (the default) the dense rows' product splits K over
+    a scratch buffer of twell_spmm_workspace_size bytes: `workspace` when
+    given, else one allocated here; without it the library gets none."""
     dev = hy.values.device
     hy.validate(dev)
     dff, dm = w_down.shape
@@ -391,10 +399,24 @@ def twell_spmm(hy: Hybrid, w_down: torch.Tensor, out: Optional[torch.Tensor] = N
         out = torch.empty((hy.n_rows, dm), dtype=hy.dtype, device=dev)
     _need(out, "y", dev, hy.dtype, (hy.n_rows, dm))
     shape = make_shape(hy.n_rows, dm, hy.d_ff, hy.tile, hy.capacity, hy.dtype)
+    lib = load()
+    ws_ptr, ws_bytes = None, 0
+    if use_workspace:
+        need = lib.twell_spmm_workspace_size(ctypes.byref(shape))
+        if workspace is None and need > 0:
+            workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            _need(workspace, "workspace", dev, torch.uint8)
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel()
     hs = hy.struct()
-    _check(load().twell_spmm(ctypes.byref(shape), ctypes.byref(hs), _ptr(w_down), _ptr(out),
-                             _stream(dev)), "twell_spmm")
+    _check(lib.twell_spmm(ctypes.byref(shape), ctypes.byref(hs), _ptr(w_down), _ptr(out), ws_ptr,
+                          ws_bytes, _stream(dev)), "twell_spmm")
     return out
+
+
+def spmm_workspace_bytes(shape: "Shape") -> int:
+    """twell_spmm_workspace_size: bytes of twell_spmm's optional workspace."""
+    return int(load().twell_spmm_workspace_size(ctypes.byref(shape)))
 
 
 # ------------------------------------------------------------------ ELL rows

@@ -303,8 +303,9 @@ def time_conversions(cfg, steps, warmup, flush, dev, t=None):
 # slot budget per row (width = d_ff / T * C, the hybrid split for rows over
 # it) and pure TwELL (panel b, C = T: no row ever overflows).  For each: the
 # rows sent to the dense matrix, the sparse down-projection of the packed h
-# (twell_spmm / ell_spmm, dense rows included: these standalone calls take no
-# workspace, so their dense fallback cannot split K), the pack from a
+# (twell_spmm with its workspace, so that its dense fallback splits K as the
+# forward's does; ell_spmm, which takes no workspace, so its fallback cannot
+# split K; dense rows included in both), the pack from a
 # materialised h, and for TwELL the whole fused forward and its own
 # down-projection (steps 3 + 4, whose fallback may split K in the forward's
 # workspace).  Cold cache, median of `steps`.
@@ -350,9 +351,12 @@ def time_formats(cfg, steps, flush, dev, caps=FORMAT_CAPACITIES):
             lambda: twell.twell_pack(h, cfg.tile, C, out=hy, workspace=ws, status=st),
             steps, warm, flush))
         y = torch.empty((cfg.n_rows, cfg.d_model), dtype=cfg.torch_dtype, device=dev)
-        row["twell_spmm_ms"] = median(_timed_calls(lambda: twell.twell_spmm(hy, d["w_down"], out=y),
-                                                   steps, warm, flush))
-        del bufs, hy, ws
+        sws = torch.empty((max(twell.spmm_workspace_bytes(twell.make_shape(
+            cfg.n_rows, cfg.d_model, cfg.d_ff, cfg.tile, C, cfg.torch_dtype)), 1),),
+            dtype=torch.uint8, device=dev)
+        row["twell_spmm_ms"] = median(_timed_calls(
+            lambda: twell.twell_spmm(hy, d["w_down"], out=y, workspace=sws), steps, warm, flush))
+        del bufs, hy, ws, sws
         if C == cfg.tile:
             out["pure_twell"] = row
             continue

@@ -282,14 +282,29 @@ int twell_unpack(const twell_shape* shape, const twell_hybrid* in, void* h, void
  * of y is written once: a row listed among the stored dense rows
  * (dense_rows[0 .. min(*n_dense, dense_capacity)), strictly ascending) by the
  * fallback only, every other row by the sparse kernel from its slots (a row
- * with no stored slot gets +0.0).
+ * with no stored slot gets +0.0).  workspace / workspace_bytes: NULL / 0, or
+ * a buffer of at least twell_spmm_workspace_size(shape) bytes for the dense
+ * rows' split-K partial sums (smaller: TWELL_ERR_WORKSPACE; not 16-byte
+ * aligned: TWELL_ERR_INVALID_ARG).  y is the same either way to within the
+ * order of the fp32 additions of the dense rows.
  * Defined by: "The Relentless Search for Efficiency in Large-Scale Language
  * Models", section "Mechanism of Action: Kernel-Level Optimization" (only the
  * weight rows of non-zero activations are read); "Nvidia and Sakana make
  * LLMs 30% faster by doing less math", section "Reshaping math for the GPU"
  * (the dense matrix as a safety valve for overflowing tokens). */
 int twell_spmm(const twell_shape* shape, const twell_hybrid* in, const void* w_down, void* y,
-               void* stream);
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the optional twell_spmm workspace for this shape (0 when none
+ * would be used; the call accepts NULL in any case).  Given, it holds the
+ * fp32 partial sums of a split of the dense rows' K (d_ff) over many
+ * workgroups, as the forward's own fallback does: at most 64 rows, the
+ * split-K kernels; bf16 past that, up to 32 K slices of the live rows, at
+ * most 32 MiB.  Without it the fallback runs one workgroup per output tile
+ * over the whole of K, which leaves most of the GPU idle when there are few
+ * dense rows.  Any 16-byte-aligned device buffer of at least this size;
+ * its contents are scratch, and calls that share one on one GPU race. */
+size_t twell_spmm_workspace_size(const twell_shape* shape);
 
 /* ---- ELL rows: Figure 1(a) beside TwELL (Figure 1(b)) and the hybrid
  * (Figure 1(c)) of "Sparser, Faster, Lighter Transformer Language Models

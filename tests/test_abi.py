@@ -58,6 +58,10 @@ def test_version_and_status_strings(lib):
     assert twell.status_string(12345) == "unknown status"
 
 
+def partials_d(rows_bucket, cols):
+    return 32 * rows_bucket * cols * 4
+
+
 def test_workspace_sizes(lib):
     s = twell.make_shape(4096, 2048, 8192, 128, 4, __import__("torch").bfloat16)
     ws = twell.ffn_workspace_bytes(s)
@@ -77,6 +81,15 @@ def test_workspace_sizes(lib):
     t = twell.make_shape(40, 136, 768, 128, 4, __import__("torch").bfloat16)  # 32 < 40 <= 64 rows
     partials = 32 * 64 * 768 * 4
     assert twell.ffn_workspace_bytes(t) == twell.pack_workspace_bytes(t) + 40 * 768 * 2 + partials
+    # twell_spmm's optional workspace: the split-K partial sums of at most 64
+    # rows (as the forward's), else bf16 32 K slices of every row, at most 32 MiB
+    assert twell.spmm_workspace_bytes(d) == partials_d(16, 16384)
+    assert twell.spmm_workspace_bytes(t) == 32 * 64 * 768 * 4
+    assert twell.spmm_workspace_bytes(s) == 32 << 20
+    small = twell.make_shape(333, 256, 1024, 128, 4, __import__("torch").bfloat16)
+    assert twell.spmm_workspace_bytes(small) == 32 * 333 * 256 * 4
+    f32 = twell.make_shape(300, 256, 1024, 128, 4, __import__("torch").float32)
+    assert twell.spmm_workspace_bytes(f32) == 0
     bad = twell.make_shape(16, 2048, 8192, 100, 4, __import__("torch").bfloat16)
     assert twell.ffn_workspace_bytes(bad) == 0
 
@@ -114,7 +127,8 @@ def test_null_arguments_rejected_on_host(lib):
     h_nodense = twell.HybridStruct(1, 1, 1, None, None, 1, 5)  # capacity 5, no buffers
     assert lib.twell_unpack(ctypes.byref(s), ctypes.byref(h_nodense), 1, None) == \
         twell.TWELL_ERR_INVALID_ARG
-    assert lib.twell_spmm(None, ctypes.byref(h), 1, 1, None) == twell.TWELL_ERR_INVALID_ARG
+    assert lib.twell_spmm(None, ctypes.byref(h), 1, 1, None, 0, None) == \
+        twell.TWELL_ERR_INVALID_ARG
 
 
 @no_gpu_only
@@ -127,6 +141,13 @@ def test_workspace_too_small_rejected_on_host(lib):
     assert rc == twell.TWELL_ERR_WORKSPACE
     rc = lib.twell_pack(ctypes.byref(s), a, ctypes.byref(h), a, 16, None, None)
     assert rc == twell.TWELL_ERR_WORKSPACE
+    # twell_spmm: no workspace is fine; a given one must be large enough
+    need = lib.twell_spmm_workspace_size(ctypes.byref(s))
+    assert need > 16
+    rc = lib.twell_spmm(ctypes.byref(s), ctypes.byref(h), a, a, a, 16, None)
+    assert rc == twell.TWELL_ERR_WORKSPACE
+    rc = lib.twell_spmm(ctypes.byref(s), ctypes.byref(h), a, a, a + 8, need, None)
+    assert rc == twell.TWELL_ERR_INVALID_ARG
     # a misaligned pointer is rejected before the size check
     rc = lib.twell_pack(ctypes.byref(s), a + 2, ctypes.byref(h), a, 1 << 30, None, None)
     assert rc == twell.TWELL_ERR_INVALID_ARG

@@ -118,11 +118,14 @@ def test_pack_zero_rows():
 
 
 # ------------------------------------------------------------------------ spmm
+@pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("n,dm,T,C", [(50, 136, 64, 4), (300, 520, 128, 4), (130, 64, 256, 8),
                                       (70, 2048, 128, 4), (33, 4096, 64, 2), (20, 8192, 256, 8)])
-def test_spmm_integer_exact(dtype, n, dm, T, C):
-    say(f"spmm integer {dtype} n={n} dm={dm} T={T}")
+def test_spmm_integer_exact(dtype, n, dm, T, C, use_ws):
+    """With and without twell_spmm's workspace (the dense rows' K split over
+    workgroups into partial sums, or one workgroup per output tile)."""
+    say(f"spmm integer {dtype} n={n} dm={dm} T={T} workspace={use_ws}")
     rng = np.random.default_rng(n + dm)
     dff = 3 * T
     h = rng.integers(-2, 3, size=(n, dff)).astype(np.float32)
@@ -130,7 +133,7 @@ def test_spmm_integer_exact(dtype, n, dm, T, C):
     w = rng.integers(-1, 2, size=(dff, dm)).astype(np.float32)
     w[rng.random((dff, dm)) < 0.7] = 0
     hy, _ = twell.twell_pack(torch.from_numpy(h).to(DT[dtype]).cuda(), T, C)
-    y = twell.twell_spmm(hy, torch.from_numpy(w).to(DT[dtype]).cuda())
+    y = twell.twell_spmm(hy, torch.from_numpy(w).to(DT[dtype]).cuda(), use_workspace=use_ws)
     torch.cuda.synchronize()
     ref_h = assert_pack_matches(hy, h)
     assert ref_h.n_dense > 0 and ref_h.n_dense < n
@@ -181,6 +184,33 @@ def test_spmm_whole_wave_rows_integer_exact(n, dm, dff, C):
     assert 0 < ref_h.n_dense < n
     y_ref = oracle.spmm(ref_h, w.astype(np.float64))
     assert np.max(np.abs(y_ref)) <= 256
+    np.testing.assert_array_equal(as_f64(y), y_ref)
+
+
+@pytest.mark.parametrize("n,dm,dff,rate", [(16, 4096, 16384, 0.008), (4096, 2048, 8192, 0.011),
+                                            (4096, 2048, 8192, 0.006)])
+def test_spmm_workspace_split_integer_exact(n, dm, dff, rate):
+    """twell_spmm with its workspace on the decode and 1B shapes: few and many
+    dense rows, so the fallback's K split ranges from 2 to 32 slices (and the
+    split-K kernels of at most 64 rows); y the same as without the workspace
+    and as the oracle, exactly (integer values)."""
+    say(f"spmm workspace split n={n} dm={dm} dff={dff} rate={rate}")
+    T, C = 128, 4
+    rng = np.random.default_rng(n + dff + int(rate * 1000))
+    h = rng.integers(-2, 3, size=(n, dff)).astype(np.float32)
+    h[rng.random((n, dff)) >= rate] = 0
+    w = rng.integers(-1, 2, size=(dff, dm)).astype(np.float32)
+    w[rng.random((dff, dm)) < 0.9] = 0
+    wd = torch.from_numpy(w).to(torch.bfloat16).cuda()
+    hy, _ = twell.twell_pack(torch.from_numpy(h).to(torch.bfloat16).cuda(), T, C)
+    y = twell.twell_spmm(hy, wd)
+    y0 = twell.twell_spmm(hy, wd, use_workspace=False)
+    torch.cuda.synchronize()
+    ref_h = assert_pack_matches(hy, h)
+    assert 0 < ref_h.n_dense < n
+    np.testing.assert_array_equal(u32(as_f32(y)), u32(as_f32(y0)))
+    y_ref = oracle.spmm(ref_h, w.astype(np.float64))
+    assert np.max(np.abs(y_ref)) <= 256  # every partial sum exact in fp32, the result in bf16
     np.testing.assert_array_equal(as_f64(y), y_ref)
 
 
@@ -463,9 +493,8 @@ def test_forward_zero_rows():
 def test_forward_matches_standalone_pack_and_spmm():
     """The fused path's hybrid equals pack(h) bit for bit, and its y equals
     twell_spmm of that hybrid bit for bit on the sparse rows; on the dense
-    rows within tolerance (the forward may split the fallback's K over
-    workgroups, keeping partial sums in its workspace, where twell_spmm has
-    none), both against the oracle."""
+    rows within tolerance (the two may split the fallback's K differently,
+    with partial sums in different workspaces), both against the oracle."""
     cfg = CONFIGS["ffn_1b_bf16"].replace(n_rows=333, d_model=256, d_ff=1024)
     t = make_inputs(cfg)
     out = run_forward(cfg, t)
@@ -536,8 +565,8 @@ def test_forward_fp32_small_batch_matches_timed_and_standalone(n_rows, d_model, 
     per wave), the event-timed variant as its own 16-range kernel. y is the
     same bits both ways; twell_spmm on the standalone pack of the same h gives
     the same bits on the sparse rows (one and several column chunks and tiles
-    per range) and runs the dense rows through its own fallback kernel, having
-    no workspace for split-K partial sums (checked against the oracle)."""
+    per range) and runs the dense rows through its own fallback launch
+    (checked against the oracle)."""
     cfg = CONFIGS["tiny_fp32"].replace(n_rows=n_rows, d_model=d_model, d_ff=d_ff)
     say(f"fp32 small batch n={n_rows} dm={d_model} dff={d_ff}")
     t = make_inputs(cfg)
