@@ -152,8 +152,14 @@ __device__ __forceinline__ int compact_row(const uint16_t* __restrict__ vals,
 #pragma unroll
       for (int i = 0; i < SPL; ++i) li[i] = idx[s0 + sb + i], lv[i] = vals[s0 + sb + i];
     }
+    if (C % SPL == 0) {  // the lane's slots are in one tile: one count
+      const uint8_t c1 = cnt[n * nt + sb / C];
 #pragma unroll
-    for (int i = 0; i < SPL; ++i) lc[i] = cnt[n * nt + (sb + i) / C];
+      for (int i = 0; i < SPL; ++i) lc[i] = c1;
+    } else {
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) lc[i] = cnt[n * nt + (sb + i) / C];
+    }
     bool live[SPL];
     int mine = 0;
 #pragma unroll
