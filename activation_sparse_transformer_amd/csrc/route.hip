@@ -399,8 +399,9 @@ __global__ __launch_bounds__(kRowThreads) void materialize_listed_kernel(
       const int u = __shfl_up(c, o, kWave);
       if (lane >= o) c += u;
     }
+    // s_off[b]: the dense rows in blocks 0 .. b-1 (s_off[nb]: all of them)
     if (lane == 0) s_off[0] = 0;
-    if (lane < nb) s_off[lane + 1] = c;  // inclusive: offsets of the blocks above
+    if (lane < nb) s_off[lane + 1] = c;
   }
   __syncthreads();
   const int n_dense = s_off[nb];
