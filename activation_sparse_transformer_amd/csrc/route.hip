@@ -757,8 +757,11 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   }
   const bool in_lds = full_src == nullptr && row_bytes <= 64 * 1024;
   const size_t lds = in_lds ? row_bytes : 0;
-  if (rmode == 2) {
-    // workgroups for the row blocks' lists and the dense rows only
+  if (rmode == 2 && full_src == nullptr) {
+    // workgroups for the row blocks' lists and the dense rows only (a copy
+    // from h, in twell_pack, keeps one workgroup per row: its dense rows are
+    // most rows, and a workgroup that copies several rows one after another
+    // was slower: 545 against 532 us at 16384 x 28672)
     const int64_t nb = (g.n_rows + kRowThreads - 1) / kRowThreads;
     const int64_t want = g.n_rows < kListedGrid ? g.n_rows : kListedGrid;
     const unsigned lblocks = static_cast<unsigned>(want > nb ? want : nb);
@@ -789,8 +792,9 @@ hipError_t launch_materialize(const Geometry& g, int elem_bytes, const int32_t* 
   };
   typedef std::integral_constant<bool, true> Yes;
   typedef std::integral_constant<bool, false> No;
-  auto by_route = [&](auto tag, auto lds_tag) {  // (route mode 2 returned above)
+  auto by_route = [&](auto tag, auto lds_tag) {
     if (rmode == 1) go(tag, lds_tag, std::integral_constant<int, 1>{});
+    else if (rmode == 2) go(tag, lds_tag, std::integral_constant<int, 2>{});
     else go(tag, lds_tag, std::integral_constant<int, 0>{});
   };
   auto by_lds = [&](auto tag) {
