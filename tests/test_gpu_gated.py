@@ -42,6 +42,8 @@ def ref(t):
     (1000, 384, 1536, 128, 6, "fp32", -1.645, 0.5),
     (129, 1024, 512, 128, 16, "bf16", -2.326, 0.0),
     (90, 4096, 1024, 128, 4, "bf16", -2.326, 0.5),
+    (600, 512, 4096, 128, 4, "bf16", -2.326, 0.5),   # the up branch mapped by XCD
+    (600, 512, 4096, 128, 4, "fp32", -2.326, 0.5),
 ])
 def test_gated_matches_oracle(n, dm, dff, T, C, dtype, b0, tsv):
     say(f"gated forward {dtype} n={n} dm={dm} dff={dff} T={T} C={C}")
@@ -73,10 +75,14 @@ def integer_case(seed, n, dm, dff, b0, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("n,b0", [(700, -10), (40, -10), (257, -11)])
-def test_gated_integer_valued_exact(dtype, n, b0):
-    dm, dff, T, C = 512, 2048, 128, 4
-    say(f"gated integer-valued {dtype} n={n} b0={b0}")
+@pytest.mark.parametrize("n,b0,dff", [(700, -10, 2048), (40, -10, 2048), (257, -11, 2048),
+                                      (700, -10, 4096)])
+def test_gated_integer_valued_exact(dtype, n, b0, dff):
+    """Exact h and y; the up branch's work mapped by XCD (a row's 16 or 32
+    tiles in eighths, at least 8 dense chunks: float32 at d_ff 2048, both
+    types at 4096) and in 64-slot parts (bfloat16 at 2048)."""
+    dm, T, C = 512, 128, 4
+    say(f"gated integer-valued {dtype} n={n} b0={b0} dff={dff}")
     t = integer_case(n * 3 + b0, n, dm, dff, b0, dtype)
     out = run(t, T, C)
     h_ref, y_ref = ref(t)
