@@ -206,15 +206,16 @@ __device__ __forceinline__ void mfma_mainloop(
 }
 
 // ============================================================ fast path
-// For K a multiple of 64.  Both operand tiles live in LDS as rows of 64
+// For K a multiple of 64.  K-major operand tiles live in LDS as rows of 64
 // K-elements (128 B) without padding; the 16-byte chunk kc of row r sits at
-// chunk position kc ^ swz(r), so the 16 rows read by one MFMA fragment load
-// fall on distinct banks.  A K-major operand is copied global -> LDS by
-// global_load_lds_dwordx4 (no VGPR staging): one instruction of a wave fills
-// one 1 KB block = 8 rows, and lane l fetches the global chunk that belongs at
-// LDS position l.  A [K][N] operand (w_down) goes through registers and is
-// transposed 4x8 on the way into LDS.  Two LDS stages, 8 waves (2 per SIMD),
-// one barrier per 64-wide K step.
+// chunk position kc ^ swz(r) for fragments of 32 rows x 2 chunks (32x32x16
+// MFMA) and kc ^ swz16(r) for fragments of 16 rows x 4 chunks (16x16x32), so
+// that a wave's fragment load has no LDS bank conflicts.  A K-major operand is
+// copied global -> LDS by global_load_lds_dwordx4 (no VGPR staging): one
+// instruction of a wave fills one 1 KB block = 8 rows, and lane l fetches the
+// global chunk that belongs at LDS position l.  A [K][N] operand (w_down) is
+// copied as stored, with 32-byte chunks swizzled by row, and read with LDS
+// transpose loads.  Two LDS stages, one barrier per 64-wide K step.
 namespace fast {
 
 constexpr int BKF = 64;
@@ -222,6 +223,10 @@ constexpr int BKF = 64;
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // element offset of (row r, 16-byte chunk kc) inside a swizzled operand tile
 __device__ __forceinline__ int tofs(int r, int kc) { return r * BKF + ((kc ^ swz(r)) << 3); }
+// Swizzle for operands read as 16-row fragments (16x16x32 MFMA: a wave's read
+// covers 16 rows x 4 chunks): row bits 1, 2, 3 go to chunk bits 0, 2, 1.
+__device__ __forceinline__ int swz16(int r) { return ((r >> 1) & 1) | (r & 4) | ((r >> 2) & 2); }
+__device__ __forceinline__ int tofs16(int r, int kc) { return r * BKF + ((kc ^ swz16(r)) << 3); }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct Cfg {
@@ -240,7 +245,7 @@ struct Cfg {
 // Global source of the chunk each lane fetches for DMA instruction i of a
 // K-major operand (rows r0.., clamped to nrows-1: rows past the end feed only
 // outputs that are never stored).
-template <int ISSUE, int NW>
+template <int ISSUE, int NW, bool SW16 = false>
 __device__ __forceinline__ void dma_sources(const uint16_t* __restrict__ base, int64_t ld, int nrows,
                                             int r0, const uint16_t* (&src)[ISSUE]) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
@@ -248,7 +253,7 @@ __device__ __forceinline__ void dma_sources(const uint16_t* __restrict__ base, i
   for (int i = 0; i < ISSUE; ++i) {
     const int blk = wave + NW * i;
     const int r = blk * 8 + lane / 8;
-    const int kc = (lane & 7) ^ swz(r);
+    const int kc = (lane & 7) ^ (SW16 ? swz16(r) : swz(r));
     const int gr = min(r0 + r, nrows - 1);
     src[i] = base + static_cast<int64_t>(gr) * ld + kc * 8;
   }
@@ -552,7 +557,7 @@ __device__ __forceinline__ void mainloop_kn(const uint16_t* __restrict__ A, int6
     for (int j = 0; j < CF::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint16_t* asrc[CF::A_ISSUE];
   const uint16_t* bsrc[B_ISSUE];
-  dma_sources<CF::A_ISSUE, CF::NW>(A, lda, M, m0, asrc);
+  dma_sources<CF::A_ISSUE, CF::NW, true>(A, lda, M, m0, asrc);
   dma_sources_kn<CF::BN, B_ISSUE, CF::NW>(B, ldb, N, n0, bsrc);
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int wm = wave / CF::WAVES_N, wn = wave % CF::WAVES_N;
@@ -577,7 +582,7 @@ __device__ __forceinline__ void mainloop_kn(const uint16_t* __restrict__ A, int6
       bf16x8_t a[CF::FM], b[CF::FN];
 #pragma unroll
       for (int i = 0; i < CF::FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(sA + tofs(wm * CF::WTM + i * 16 + (lane & 15), kc));
+        a[i] = *reinterpret_cast<const bf16x8_t*>(sA + tofs16(wm * CF::WTM + i * 16 + (lane & 15), kc));
 #pragma unroll
       for (int j = 0; j < CF::FN; ++j)
         b[j] = tr_fragment<CF::BN>(sB, ks * 32 + (lane >> 4) * 8, wn * CF::WTN + j * 16);
